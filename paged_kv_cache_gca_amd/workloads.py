@@ -1,0 +1,66 @@
+"""Synthetic GCA workloads shaped like the lingbot-map pages' streaming runs.
+
+Frames are 518x378 images cut into 14x14 patches (37 x 27 = 999 patch tokens)
+plus 5 special tokens, i.e. 1004 tokens per frame; the global attention uses
+16 heads of width 64 (embed_dim 1024).  Stream lengths, window sizes and
+keyframe intervals follow the runs the pages describe: 1,000-frame sequences
+with a 64-frame window, 10,000-frame streams with keyframe-only caching, and
+a strict 12-frame sliding window (current frame + 11 cached frames).
+
+Only parameters live here; no arithmetic of the method.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    T: int              # tokens per frame
+    H: int              # heads
+    D: int              # head dim
+    P: int              # page size (tokens)
+    dtype: str          # "f32" | "bf16"
+    n_frames: int       # frames in the stream
+    A: int              # anchor frames
+    W: int              # window keyframes (incl. the newest)
+    C: int              # compact tokens kept per evicted frame
+    rope: int           # 0 none, 1 3D (t, h, w)
+    num_special: int
+    grid_h: int
+    grid_w: int
+    keyframe_interval: int = 1
+    n_base: int | None = None      # distinct base frames cycled (None: every frame distinct)
+    drift_sigma: float = 0.0
+    seed: int = 1
+
+    @property
+    def n_keyframes(self) -> int:
+        return (self.n_frames + self.keyframe_interval - 1) // self.keyframe_interval
+
+    def is_keyframe(self, f: int) -> bool:
+        return f % self.keyframe_interval == 0
+
+
+TINY_F32 = Workload("tiny_f32_T64_H2", T=64, H=2, D=64, P=16, dtype="f32", n_frames=6,
+                    A=1, W=2, C=1, rope=0, num_special=0, grid_h=8, grid_w=8, seed=1)
+
+FRAME1004_W16 = Workload("bf16_T1004_H16_P16_W16_64f", T=1004, H=16, D=64, P=16, dtype="bf16",
+                         n_frames=64, A=1, W=16, C=13, rope=1, num_special=5,
+                         grid_h=27, grid_w=37, seed=2)
+
+STREAM1000_W64 = Workload("bf16_T1004_H16_P64_W64_1000f", T=1004, H=16, D=64, P=64, dtype="bf16",
+                          n_frames=1000, A=1, W=64, C=13, rope=1, num_special=5,
+                          grid_h=27, grid_w=37, n_base=64, seed=3)
+
+STREAM10K_KF4 = Workload("bf16_T1004_H16_P64_W32_10000f_kf4", T=1004, H=16, D=64, P=64,
+                         dtype="bf16", n_frames=10000, A=1, W=32, C=13, rope=1, num_special=5,
+                         grid_h=27, grid_w=37, keyframe_interval=4, n_base=64,
+                         drift_sigma=0.1, seed=4)
+
+RING20K_W12 = Workload("bf16_T1004_H16_P64_ring12_20000f", T=1004, H=16, D=64, P=64,
+                       dtype="bf16", n_frames=20000, A=0, W=12, C=0, rope=1, num_special=5,
+                       grid_h=27, grid_w=37, n_base=64, seed=5)
+
+ALL = [TINY_F32, FRAME1004_W16, STREAM1000_W64, STREAM10K_KF4, RING20K_W12]
