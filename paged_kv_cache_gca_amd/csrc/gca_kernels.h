@@ -1,0 +1,106 @@
+// Kernel argument blocks and launchers shared by the GCA runtime and kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace gca {
+
+constexpr int kHeadDim = 64;    // D
+constexpr int kKeysPerTile = 64;  // keys staged in LDS per attention step
+constexpr int kWaves = 4;       // waves per attention workgroup
+// queries per attention workgroup: 4 waves x 64 (bf16) or x 32 (float32)
+inline int queries_per_wg(int dtype) { return kWaves * (dtype ? 64 : 32); }
+constexpr int kNumXcd = 8;      // MI355X: 8 accelerator complex dies, round-robin dispatch
+
+// Rotary tables: (cos, sin) in float32, evaluated in float64 on the host.
+struct RopeTabs {
+  const float2* t;  // [max_frames][nt]
+  const float2* h;  // [grid_h][nh]
+  const float2* w;  // [grid_w][nw]
+  int nt, nh, nw;   // rotation pairs per axis block (time, row, column)
+  int num_special, grid_w;
+};
+
+struct AppendArgs {
+  const void* k;
+  const void* v;
+  void* kpool;  // [N][H][P][D]
+  void* vpool;  // [N][H][D][P]
+  const int32_t* ring;
+  int32_t* rec_pages;  // [slots][ppf]
+  int64_t ring_pos;
+  int64_t frame;
+  int N, slot, ppf, T, H, P;
+  int rope;
+  RopeTabs tabs;
+};
+
+struct EvictArgs {
+  void* kpool;
+  void* vpool;
+  int32_t* ring;
+  const int32_t* rec_pages;
+  int32_t* traj_pages;
+  const int32_t* compact;
+  int64_t traj_len, ring_head, ring_tail;
+  int N, slot, ppf, n_traj_pages, new_pages, C, H, P;
+};
+
+struct SelectArgs {
+  const int32_t* rec_pages;
+  const int32_t* traj_pages;
+  int32_t* sel_page;
+  int32_t* sel_len;
+  int64_t traj_len;
+  int ppf, P, last_len, A, Wr, n_anchor, win_first, win_count, n_traj_pages, n_sel;
+};
+
+struct AttnArgs {
+  const void* q;       // raw [Tq][H][D]
+  const void* kpool;   // [N][H][P][D]
+  const void* vpool;   // [N][H][D][P]
+  const int32_t* sel_page;
+  const int32_t* sel_len;
+  float* o_part;       // [S][Tq][H][D] (S > 1)
+  float* lse_part;     // [S][Tq][H]
+  void* out;           // [Tq][H][D] (S == 1)
+  float* lse;          // [Tq][H] or null (S == 1)
+  int64_t frame;
+  float sm_scale;      // > 0
+  float c2;            // sm_scale * log2(e)
+  int Tq, H, P, n_sel, n_tiles, tiles_per_split, S, n_qtiles, n_units;
+  int out_bf16;
+  int rope;
+  RopeTabs tabs;
+};
+
+struct MergeArgs {
+  const float* o_part;
+  const float* lse_part;
+  void* out;
+  float* lse;
+  int rows;  // Tq * H
+  int S;
+  int out_bf16;
+};
+
+struct RopeArgs {
+  const void* x;
+  void* y;
+  int64_t frame;
+  int T, H;
+  RopeTabs tabs;
+};
+
+// Launchers (defined in gca_kernels.hip).  dtype: 0 float32, 1 bfloat16.
+hipError_t launch_append(int dtype, const AppendArgs& a, hipStream_t s);
+hipError_t launch_evict(int dtype, const EvictArgs& a, hipStream_t s);
+hipError_t launch_select(const SelectArgs& a, hipStream_t s);
+hipError_t launch_attn(int dtype, const AttnArgs& a, hipStream_t s);
+hipError_t launch_merge(const MergeArgs& a, hipStream_t s);
+hipError_t launch_rope(int dtype, const RopeArgs& a, hipStream_t s);
+hipError_t launch_ring_init(int32_t* ring, const int32_t* init, int N, hipStream_t s);
+
+}  // namespace gca

@@ -1,0 +1,606 @@
+// HIP kernels of the GCA path for CDNA4 (gfx950, MI355X).
+//
+//   k_rope    3D (t, h, w) rotary embedding of a [T][H][D] tensor
+//   k_append  pop a frame's pages, rotate K, scatter K into [page][H][P][D]
+//             and V transposed into [page][H][D][P]
+//   k_evict   copy an evicted frame's compact tokens into trajectory pages
+//             and push the frame's pages to the ring tail
+//   k_select  gather list (page, valid tokens): anchor, window, trajectory
+//   k_attn    paged flash attention: K/V pages staged in LDS, S^T = K Q^T and
+//             O^T = V^T P^T on MFMA (bf16 32x32x16, or f32 32x32x2), online
+//             softmax in float32, split over the context (split-KV)
+//   k_merge   log-sum-exp merge of the split partials
+//
+// Ring positions, record slots and sizes arrive as launch arguments computed by
+// the host planner; page ids are read from and written to device memory only.
+#include "gca_kernels.h"
+
+namespace gca {
+namespace {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+template <typename T>
+union Vec16 {
+  uint4 u;
+  T e[16 / sizeof(T)];
+};
+
+__device__ inline float to_f(float x) { return x; }
+__device__ inline float to_f(bf16 x) { return (float)x; }
+template <typename T>
+__device__ inline T from_f(float x);
+template <>
+__device__ inline float from_f<float>(float x) { return x; }
+template <>
+__device__ inline bf16 from_f<bf16>(float x) { return (bf16)x; }  // round to nearest even
+
+// ---------------------------------------------------------------------------
+// 3D rotary embedding.  Pair j rotates dims (2j, 2j+1); pairs [0, nt) use the
+// frame index, [nt, nt+nh) the patch row, the rest the patch column; special
+// tokens sit at row 0, column 0.
+
+__device__ inline float2 rope_cs(const RopeTabs& R, int64_t frame, int tok, int pair) {
+  if (pair < R.nt) return R.t[frame * R.nt + pair];
+  int row = 0, col = 0;
+  if (tok >= R.num_special) {
+    int p = tok - R.num_special;
+    row = p / R.grid_w;
+    col = p - row * R.grid_w;
+  }
+  pair -= R.nt;
+  if (pair < R.nh) return R.h[row * R.nh + pair];
+  return R.w[col * R.nw + (pair - R.nh)];
+}
+
+// One fixed operation sequence, so every kernel that rotates gives the same bits.
+__device__ inline void rotate(float x0, float x1, float2 cs, float& y0, float& y1) {
+  float a = x1 * cs.y;
+  float b = x1 * cs.x;
+  y0 = __builtin_fmaf(x0, cs.x, -a);
+  y1 = __builtin_fmaf(x0, cs.y, b);
+}
+
+template <typename T>
+__device__ inline void rotate_chunk(Vec16<T>& v, const RopeTabs& R, int64_t frame, int tok,
+                                    int first_pair) {
+  constexpr int EPC = 16 / sizeof(T);
+#pragma unroll
+  for (int m = 0; m < EPC / 2; ++m) {
+    float2 cs = rope_cs(R, frame, tok, first_pair + m);
+    float y0, y1;
+    rotate(to_f(v.e[2 * m]), to_f(v.e[2 * m + 1]), cs, y0, y1);
+    v.e[2 * m] = from_f<T>(y0);
+    v.e[2 * m + 1] = from_f<T>(y1);
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void k_rope(RopeArgs a) {
+  constexpr int EPC = 16 / sizeof(T);
+  constexpr int CPR = kHeadDim / EPC;
+  size_t c = (size_t)blockIdx.x * 256 + threadIdx.x;
+  size_t total = (size_t)a.T * a.H * CPR;
+  if (c >= total) return;
+  int part = (int)(c % CPR);
+  int tok = (int)(c / CPR / a.H);
+  Vec16<T> v;
+  v.u = ((const uint4*)a.x)[c];
+  rotate_chunk<T>(v, a.tabs, a.frame, tok, part * EPC / 2);
+  ((uint4*)a.y)[c] = v.u;
+}
+
+// ---------------------------------------------------------------------------
+// Append: workgroup (i, h) fills page i of the frame for head h.  K rows are
+// rotated and written token-major; V goes through LDS and is written
+// dim-major (V^T), the operand layout of the P.V contraction.  Slots past the
+// frame's last token are zeroed.
+
+template <typename T>
+__global__ __launch_bounds__(256) void k_append(AppendArgs a) {
+  constexpr int EPC = 16 / sizeof(T);
+  constexpr int CPR = kHeadDim / EPC;
+  constexpr int LP = kHeadDim + EPC;  // LDS row pitch
+  __shared__ __attribute__((aligned(16))) T lds[64 * LP];
+  const int i = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+  const int page = a.ring[(a.ring_pos + i) % a.N];
+  if (h == 0 && tid == 0) a.rec_pages[a.slot * a.ppf + i] = page;
+  const T* K = (const T*)a.k;
+  const T* V = (const T*)a.v;
+  T* kp = (T*)a.kpool + ((size_t)page * a.H + h) * a.P * kHeadDim;
+  T* vp = (T*)a.vpool + ((size_t)page * a.H + h) * kHeadDim * a.P;
+  const int tok0 = i * a.P;
+  for (int c = tid; c < a.P * CPR; c += 256) {
+    int s = c / CPR, part = c - s * CPR;
+    int tok = tok0 + s;
+    Vec16<T> kv, vv;
+    kv.u = make_uint4(0, 0, 0, 0);
+    vv.u = kv.u;
+    if (tok < a.T) {
+      size_t off = ((size_t)tok * a.H + h) * kHeadDim + part * EPC;
+      kv.u = *(const uint4*)(K + off);
+      vv.u = *(const uint4*)(V + off);
+      if (a.rope) rotate_chunk<T>(kv, a.tabs, a.frame, tok, part * EPC / 2);
+    }
+    *(uint4*)(kp + (size_t)s * kHeadDim + part * EPC) = kv.u;
+    *(uint4*)(lds + s * LP + part * EPC) = vv.u;
+  }
+  __syncthreads();
+  const int cpk = a.P / EPC;  // 16-byte chunks per V^T row
+  for (int c = tid; c < kHeadDim * cpk; c += 256) {
+    int d = c / cpk, kc = c - d * cpk;
+    Vec16<T> o;
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) o.e[e] = lds[(kc * EPC + e) * LP + d];
+    *(uint4*)(vp + (size_t)d * a.P + kc * EPC) = o.u;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Evict one frame: workgroup h copies the C compact tokens of head h; block 0
+// also records the trajectory pages it pops and pushes the frame's pages to
+// the ring tail.  The popped positions [ring_head, ring_head + new_pages) and
+// pushed positions [ring_tail, ring_tail + ppf) never overlap modulo N because
+// the evicted frame's own pages are live while it is evicted.
+
+template <typename T>
+__global__ __launch_bounds__(256) void k_evict(EvictArgs a) {
+  const int h = blockIdx.x, tid = threadIdx.x;
+  T* kp = (T*)a.kpool;
+  T* vp = (T*)a.vpool;
+  for (int idx = tid; idx < a.C * kHeadDim; idx += 256) {
+    int j = idx / kHeadDim, d = idx - j * kHeadDim;
+    int tok = a.compact[j];
+    int src = a.rec_pages[a.slot * a.ppf + tok / a.P];
+    int ss = tok % a.P;
+    int64_t tt = a.traj_len + j;
+    int pi = (int)(tt / a.P);
+    int ds = (int)(tt % a.P);
+    int dst = pi < a.n_traj_pages ? a.traj_pages[pi]
+                                  : a.ring[(a.ring_head + (pi - a.n_traj_pages)) % a.N];
+    kp[(((size_t)dst * a.H + h) * a.P + ds) * kHeadDim + d] =
+        kp[(((size_t)src * a.H + h) * a.P + ss) * kHeadDim + d];
+    vp[(((size_t)dst * a.H + h) * kHeadDim + d) * a.P + ds] =
+        vp[(((size_t)src * a.H + h) * kHeadDim + d) * a.P + ss];
+  }
+  if (h == 0) {
+    for (int i = tid; i < a.new_pages; i += 256)
+      a.traj_pages[a.n_traj_pages + i] = a.ring[(a.ring_head + i) % a.N];
+    for (int i = tid; i < a.ppf; i += 256)
+      a.ring[(a.ring_tail + i) % a.N] = a.rec_pages[a.slot * a.ppf + i];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Gather list in canonical order: anchors, window oldest -> newest, trajectory.
+
+__global__ __launch_bounds__(256) void k_select(SelectArgs a) {
+  int e = blockIdx.x * 256 + threadIdx.x;
+  if (e >= a.n_sel) return;
+  int nf = (a.n_anchor + a.win_count) * a.ppf;
+  int page, len;
+  if (e < nf) {
+    int f = e / a.ppf, i = e - f * a.ppf;
+    int slot = f < a.n_anchor ? f : a.A + (a.win_first + (f - a.n_anchor)) % a.Wr;
+    page = a.rec_pages[slot * a.ppf + i];
+    len = (i == a.ppf - 1) ? a.last_len : a.P;
+  } else {
+    int ti = e - nf;
+    page = a.traj_pages[ti];
+    int64_t rem = a.traj_len - (int64_t)ti * a.P;
+    len = rem < a.P ? (int)rem : a.P;
+  }
+  a.sel_page[e] = page;
+  a.sel_len[e] = len;
+}
+
+__global__ void k_ring_init(int32_t* ring, const int32_t* init, int N) {
+  int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < N) ring[i] = init ? init[i] : i;
+}
+
+// ---------------------------------------------------------------------------
+// Paged attention.
+//
+// Workgroup = 4 waves x 64 queries of one head, over one split of the gather
+// list.  Per 64-key tile: K (64 keys x 64 dims) and V^T (64 dims x 64 keys)
+// are staged in LDS, then each wave computes S^T = K Q^T (keys x queries) with
+// 32x32 MFMA blocks, so that each lane owns one query column: the softmax max
+// and scaling are per lane plus one exchange with lane ^ 32.  P^T is fed
+// straight from the S^T accumulators as the B operand of O^T = V^T P^T; the
+// key order inside each 16-key chunk follows the accumulator layout, and the
+// V^T operand is read in the same order.  Row sums come from one more MFMA
+// with an all-ones A operand over the same rounded P, so sum(P) and P.V use
+// identical weights.
+
+template <typename T>
+struct Mfma;
+template <>
+struct Mfma<bf16> {
+  static constexpr int NQB = 2;  // 32-query blocks per wave
+  static constexpr int KPL = 8;  // operand elements per lane
+  typedef bf16x8 Frag;
+  __device__ static inline floatx16 mma(Frag a, Frag b, floatx16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+  __device__ static inline Frag ones() {
+    Frag f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) f[i] = (bf16)1.0f;
+    return f;
+  }
+};
+template <>
+struct Mfma<float> {
+  static constexpr int NQB = 1;
+  static constexpr int KPL = 1;
+  typedef float Frag;
+  __device__ static inline floatx16 mma(Frag a, Frag b, floatx16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+  }
+  __device__ static inline Frag ones() { return 1.0f; }
+};
+
+// K operand: key row `row`, dims [dc*2*KPL + hi*KPL, +KPL).
+__device__ inline bf16x8 read_k(const bf16* lk, int pitch, int row, int dc, int hi) {
+  return *(const bf16x8*)(lk + row * pitch + dc * 16 + hi * 8);
+}
+__device__ inline float read_k(const float* lk, int pitch, int row, int dc, int hi) {
+  return lk[row * pitch + dc * 2 + hi];
+}
+
+// V^T operand for dim row d and chunk ch of key block kb: the keys whose S^T
+// accumulator registers form the matching P^T operand.
+__device__ inline bf16x8 read_v(const bf16* lv, int pitch, int d, int kb, int ch, int hi) {
+  const bf16* p = lv + d * pitch + kb * 32 + ch * 16 + hi * 4;
+  bf16x4 x = *(const bf16x4*)p;
+  bf16x4 y = *(const bf16x4*)(p + 8);
+  bf16x8 r;
+  r[0] = x[0]; r[1] = x[1]; r[2] = x[2]; r[3] = x[3];
+  r[4] = y[0]; r[5] = y[1]; r[6] = y[2]; r[7] = y[3];
+  return r;
+}
+__device__ inline float read_v(const float* lv, int pitch, int d, int kb, int ch, int hi) {
+  return lv[d * pitch + kb * 32 + (ch >> 2) * 8 + hi * 4 + (ch & 3)];
+}
+
+__device__ inline bf16x8 pack_p(const floatx16& s, int ch, bf16) {
+  bf16x8 r;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r[i] = (bf16)s[ch * 8 + i];
+  return r;
+}
+__device__ inline float pack_p(const floatx16& s, int ch, float) { return s[ch]; }
+
+// Rotated queries as B operands: lane holds query qb*32 + l32, dims
+// [dc*2*KPL + hi*KPL, +KPL).
+__device__ inline void load_q(const AttnArgs& a, int qbase, int h, int l32, int hi, bf16x8 (&qf)[2][4]) {
+  const bf16* Q = (const bf16*)a.q;
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    int q = qbase + qb * 32 + l32;
+#pragma unroll
+    for (int dc = 0; dc < 4; ++dc) {
+      Vec16<bf16> v;
+      v.u = make_uint4(0, 0, 0, 0);
+      int d0 = dc * 16 + hi * 8;
+      if (q < a.Tq) {
+        v.u = *(const uint4*)(Q + ((size_t)q * a.H + h) * kHeadDim + d0);
+        if (a.rope) rotate_chunk<bf16>(v, a.tabs, a.frame, q, d0 / 2);
+      }
+      bf16x8 f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) f[i] = v.e[i];
+      qf[qb][dc] = f;
+    }
+  }
+}
+__device__ inline void load_q(const AttnArgs& a, int qbase, int h, int l32, int hi, float (&qf)[1][32]) {
+  const float* Q = (const float*)a.q;
+#pragma unroll
+  for (int qb = 0; qb < 1; ++qb) {
+    int q = qbase + qb * 32 + l32;
+#pragma unroll
+    for (int dc = 0; dc < 32; ++dc) {
+      float x = 0.f;
+      if (q < a.Tq) {
+        float2 p = *(const float2*)(Q + ((size_t)q * a.H + h) * kHeadDim + dc * 2);
+        if (a.rope) {
+          float y0, y1;
+          rotate(p.x, p.y, rope_cs(a.tabs, a.frame, q, dc), y0, y1);
+          p.x = y0;
+          p.y = y1;
+        }
+        x = hi ? p.y : p.x;
+      }
+      qf[qb][dc] = x;
+    }
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
+  using M = Mfma<T>;
+  using Frag = typename M::Frag;
+  constexpr int NQB = M::NQB;
+  constexpr int KPL = M::KPL;
+  constexpr int NDC = kHeadDim / (2 * KPL);  // MFMAs along the head dim
+  constexpr int NCH = 16 / KPL;              // P^T operands per 32-key block
+  constexpr int EPC = 16 / sizeof(T);
+  constexpr int KP = kHeadDim + EPC;         // K tile row pitch
+  constexpr int VP = kKeysPerTile + EPC;     // V^T tile row pitch
+  constexpr int QPW = NQB * 32;              // queries per wave
+  __shared__ __attribute__((aligned(16))) T lk[kKeysPerTile * KP];
+  __shared__ __attribute__((aligned(16))) T lv[kHeadDim * VP];
+  __shared__ int llen[kKeysPerTile / 16];
+
+  // workgroup -> (head, split, q tile): the q tiles of one (head, split) are
+  // consecutive on one XCD (dispatch is round-robin over XCDs), so they share
+  // that XCD's L2 copy of the split's K/V pages.
+  const int b = blockIdx.x;
+  const int xcd = b % kNumXcd, kx = b / kNumXcd;
+  const int unit = (kx / a.n_qtiles) * kNumXcd + xcd;
+  const int qt = kx % a.n_qtiles;
+  if (unit >= a.n_units) return;
+  const int h = unit / a.S, split = unit % a.S;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, hi = lane >> 5;
+  const int ept = kKeysPerTile / a.P;
+  const int t0 = split * a.tiles_per_split;
+  const int t1 = min(a.n_tiles, t0 + a.tiles_per_split);
+  const int qbase = (qt * kWaves + wave) * QPW;
+  const T* kpool = (const T*)a.kpool;
+  const T* vpool = (const T*)a.vpool;
+
+  Frag qf[NQB][NDC];
+  load_q(a, qbase, h, l32, hi, qf);
+
+  floatx16 o[2][NQB];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < NQB; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[i][j][r] = 0.f;
+  float m[NQB], l[NQB];
+#pragma unroll
+  for (int qb = 0; qb < NQB; ++qb) {
+    m[qb] = -INFINITY;
+    l[qb] = 0.f;
+  }
+  const Frag ones = M::ones();
+  const float c2 = a.c2;
+
+  for (int tile = t0; tile < t1; ++tile) {
+    __syncthreads();  // previous tile fully consumed
+    if (tid < ept) {
+      int e = tile * ept + tid;
+      llen[tid] = e < a.n_sel ? a.sel_len[e] : 0;
+    }
+    constexpr int CPRK = kHeadDim / EPC;
+    for (int c = tid; c < kKeysPerTile * CPRK; c += 256) {
+      int r = c / CPRK, part = c - r * CPRK;
+      int e = tile * ept + r / a.P;
+      int slot = r % a.P;
+      uint4 val = make_uint4(0, 0, 0, 0);
+      if (e < a.n_sel) {
+        int pg = a.sel_page[e];
+        val = *(const uint4*)(kpool + (((size_t)pg * a.H + h) * a.P + slot) * kHeadDim + part * EPC);
+      }
+      *(uint4*)(lk + r * KP + part * EPC) = val;
+    }
+    constexpr int CPRV = kKeysPerTile / EPC;
+    for (int c = tid; c < kHeadDim * CPRV; c += 256) {
+      int d = c / CPRV, kc = c - d * CPRV;
+      int k0 = kc * EPC;
+      int e = tile * ept + k0 / a.P;
+      int slot0 = k0 % a.P;
+      Vec16<T> val;
+      val.u = make_uint4(0, 0, 0, 0);
+      if (e < a.n_sel) {
+        int pg = a.sel_page[e], len = a.sel_len[e];
+        val.u = *(const uint4*)(vpool + (((size_t)pg * a.H + h) * kHeadDim + d) * a.P + slot0);
+        if (slot0 + EPC > len) {
+#pragma unroll
+          for (int i = 0; i < EPC; ++i)
+            if (slot0 + i >= len) val.e[i] = from_f<T>(0.f);
+        }
+      }
+      *(uint4*)(lv + d * VP + k0) = val.u;
+    }
+    __syncthreads();
+
+    // S^T = K Q^T: s[kb][qb] holds keys kb*32 + 8*(r/4) + 4*hi + r%4 of query column l32
+    floatx16 s[2][NQB];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[kb][qb][r] = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int dc = 0; dc < NDC; ++dc) {
+        Frag kf = read_k(lk, KP, kb * 32 + l32, dc, hi);
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb) s[kb][qb] = M::mma(kf, qf[qb][dc], s[kb][qb]);
+      }
+
+    bool full = true;
+    for (int i = 0; i < ept; ++i) full = full && (llen[i] == a.P);
+    if (!full) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          int key = kb * 32 + (r >> 2) * 8 + hi * 4 + (r & 3);
+          bool ok = (key % a.P) < llen[key / a.P];
+          if (!ok) {
+#pragma unroll
+            for (int qb = 0; qb < NQB; ++qb) s[kb][qb][r] = -INFINITY;
+          }
+        }
+    }
+
+    // online softmax, one query column per lane; P packed to MFMA operands
+    Frag pf[2][NCH][NQB];
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) {
+      float mx = s[0][qb][0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[0][qb][r]);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[1][qb][r]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      float mn = fmaxf(m[qb], mx);
+      float alpha = __builtin_amdgcn_exp2f((m[qb] - mn) * c2);
+      m[qb] = mn;
+      float mc = mn * c2;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          s[kb][qb][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][qb][r], c2, -mc));
+#pragma unroll
+        for (int ch = 0; ch < NCH; ++ch) pf[kb][ch][qb] = pack_p(s[kb][qb], ch, T());
+      }
+      o[0][qb] *= alpha;
+      o[1][qb] *= alpha;
+      l[qb] *= alpha;
+    }
+
+    // O^T += V^T P^T
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int ch = 0; ch < NCH; ++ch)
+#pragma unroll
+        for (int db = 0; db < 2; ++db) {
+          Frag vf = read_v(lv, VP, db * 32 + l32, kb, ch, hi);
+#pragma unroll
+          for (int qb = 0; qb < NQB; ++qb) o[db][qb] = M::mma(vf, pf[kb][ch][qb], o[db][qb]);
+        }
+    // row sums of the same rounded P, via an all-ones A operand
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) {
+      floatx16 lt;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) lt[r] = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int ch = 0; ch < NCH; ++ch) lt = M::mma(ones, pf[kb][ch][qb], lt);
+      l[qb] += lt[0];
+    }
+  }
+
+  // epilogue: O^T accumulators hold dims db*32 + 8*(r/4) + 4*hi + r%4
+#pragma unroll
+  for (int qb = 0; qb < NQB; ++qb) {
+    int q = qbase + qb * 32 + l32;
+    if (q >= a.Tq) continue;
+    bool empty = !(l[qb] > 0.f);
+    float inv = empty ? 0.f : 1.f / l[qb];
+    float lse = empty ? -INFINITY : m[qb] * a.sm_scale + __logf(l[qb]);
+    size_t row = (size_t)q * a.H + h;
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        int d = db * 32 + g * 8 + hi * 4;
+        floatx4 v;
+        v[0] = o[db][qb][g * 4 + 0] * inv;
+        v[1] = o[db][qb][g * 4 + 1] * inv;
+        v[2] = o[db][qb][g * 4 + 2] * inv;
+        v[3] = o[db][qb][g * 4 + 3] * inv;
+        if (a.S > 1) {
+          *(floatx4*)(a.o_part + ((size_t)split * a.Tq * a.H + row) * kHeadDim + d) = v;
+        } else if (a.out_bf16) {
+          bf16x4 w;
+          w[0] = (bf16)v[0]; w[1] = (bf16)v[1]; w[2] = (bf16)v[2]; w[3] = (bf16)v[3];
+          *(bf16x4*)((bf16*)a.out + row * kHeadDim + d) = w;
+        } else {
+          *(floatx4*)((float*)a.out + row * kHeadDim + d) = v;
+        }
+      }
+    if (hi == 0) {
+      if (a.S > 1) a.lse_part[(size_t)split * a.Tq * a.H + row] = lse;
+      else if (a.lse) a.lse[row] = lse;
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void k_merge(MergeArgs a) {
+  int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  int d = threadIdx.x & 63;
+  if (row >= a.rows) return;
+  float mx = -INFINITY;
+  for (int s = 0; s < a.S; ++s) mx = fmaxf(mx, a.lse_part[(size_t)s * a.rows + row]);
+  float sum = 0.f, acc = 0.f;
+  for (int s = 0; s < a.S; ++s) {
+    float ls = a.lse_part[(size_t)s * a.rows + row];
+    if (ls == -INFINITY) continue;
+    float w = __expf(ls - mx);
+    sum += w;
+    acc = __builtin_fmaf(w, a.o_part[((size_t)s * a.rows + row) * kHeadDim + d], acc);
+  }
+  float v = acc / sum;
+  if (a.out_bf16) ((bf16*)a.out)[(size_t)row * kHeadDim + d] = (bf16)v;
+  else ((float*)a.out)[(size_t)row * kHeadDim + d] = v;
+  if (d == 0 && a.lse) a.lse[row] = mx + __logf(sum);
+}
+
+}  // namespace
+
+hipError_t launch_append(int dtype, const AppendArgs& a, hipStream_t s) {
+  dim3 grid(a.ppf, a.H);
+  if (dtype) hipLaunchKernelGGL(k_append<bf16>, grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL(k_append<float>, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_evict(int dtype, const EvictArgs& a, hipStream_t s) {
+  dim3 grid(a.H);
+  if (dtype) hipLaunchKernelGGL(k_evict<bf16>, grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL(k_evict<float>, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_select(const SelectArgs& a, hipStream_t s) {
+  if (a.n_sel <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_select, dim3((a.n_sel + 255) / 256), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn(int dtype, const AttnArgs& a, hipStream_t s) {
+  int groups = (a.n_units + kNumXcd - 1) / kNumXcd;
+  dim3 grid(groups * kNumXcd * a.n_qtiles);
+  if (dtype) hipLaunchKernelGGL(k_attn<bf16>, grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL(k_attn<float>, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_merge(const MergeArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(k_merge, dim3((a.rows + 3) / 4), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_rope(int dtype, const RopeArgs& a, hipStream_t s) {
+  size_t chunks = (size_t)a.T * a.H * (dtype ? 8 : 16);
+  dim3 grid((unsigned)((chunks + 255) / 256));
+  if (dtype) hipLaunchKernelGGL(k_rope<bf16>, grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL(k_rope<float>, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_ring_init(int32_t* ring, const int32_t* init, int N, hipStream_t s) {
+  hipLaunchKernelGGL(k_ring_init, dim3((N + 255) / 256), dim3(256), 0, s, ring, init, N);
+  return hipGetLastError();
+}
+
+}  // namespace gca

@@ -1,0 +1,562 @@
+// Host runtime of the GCA library: the C ABI of include/gca.h.
+//
+// Every device call validates against the host planner first (no device
+// sync), enqueues its kernels on the caller's stream, and only then commits
+// the planner state, so a rejected call changes nothing.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/gca.h"
+#include "gca_kernels.h"
+#include "gca_plan.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int hip_fail(hipError_t e, const char* what) {
+  char buf[256];
+  std::snprintf(buf, sizeof buf, "%s: %s", what, hipGetErrorString(e));
+  g_last_error = buf;
+  return GCA_ERR_HIP;
+}
+
+#define GCA_HIP(call, what)                 \
+  do {                                      \
+    hipError_t e_ = (call);                 \
+    if (e_ != hipSuccess) return hip_fail(e_, what); \
+  } while (0)
+
+bool aligned16(const void* p) { return p && ((uintptr_t)p & 15) == 0; }
+
+constexpr int kMaxSplits = 16;
+
+struct ProfRec {
+  int kind;
+  hipEvent_t a, b;
+};
+
+}  // namespace
+
+struct gca_cache {
+  gca::Geometry g;
+  gca::Planner plan;
+  int device = 0;
+  int num_cu = 256;
+  size_t esize = 2;
+  void* kpool = nullptr;
+  void* vpool = nullptr;
+  int32_t* ring = nullptr;
+  int32_t* ring_init = nullptr;  // device copy of a caller order, or null
+  int32_t* rec_pages = nullptr;
+  int32_t* traj_pages = nullptr;
+  int32_t* compact = nullptr;
+  int32_t* sel_page = nullptr;
+  int32_t* sel_len = nullptr;
+  float2* rope_t = nullptr;
+  float2* rope_h = nullptr;
+  float2* rope_w = nullptr;
+  gca::RopeTabs tabs{};
+  float* o_part = nullptr;
+  float* lse_part = nullptr;
+  bool sel_valid = false;
+  int sel_n = 0;
+  int64_t sel_ctx = 0;
+  // profiling
+  int prof_cap = 0;
+  std::vector<ProfRec> prof;
+  std::vector<hipEvent_t> prof_pool;
+
+  explicit gca_cache(const gca::Geometry& geo) : g(geo), plan(geo) {}
+};
+
+namespace {
+
+void free_all(gca_cache* c) {
+  void* ptrs[] = {c->kpool, c->vpool, c->ring, c->ring_init, c->rec_pages, c->traj_pages,
+                  c->compact, c->sel_page, c->sel_len, c->rope_t, c->rope_h, c->rope_w,
+                  c->o_part, c->lse_part};
+  for (void* p : ptrs)
+    if (p) (void)hipFree(p);
+  for (auto& r : c->prof) {
+    (void)hipEventDestroy(r.a);
+    (void)hipEventDestroy(r.b);
+  }
+  for (auto e : c->prof_pool) (void)hipEventDestroy(e);
+}
+
+template <typename T>
+hipError_t dmalloc(T** p, size_t bytes) {
+  return hipMalloc((void**)p, std::max<size_t>(bytes, 16));
+}
+
+// Rotary tables for the [t | h | w] split of the head dim: d_h = d_w =
+// 2 * (D / 6), d_t = D - d_h - d_w; pair j of an axis block of width d turns
+// by pos * theta^(-2j/d).  Evaluated in double, stored as float (cos, sin).
+void build_rope(const gca::Geometry& g, std::vector<float2>* t, std::vector<float2>* h,
+                std::vector<float2>* w, int* nt, int* nh, int* nw) {
+  int dh = 2 * (g.D / 6), dw = dh, dt = g.D - dh - dw;
+  *nt = dt / 2;
+  *nh = dh / 2;
+  *nw = dw / 2;
+  auto fill = [&](std::vector<float2>* out, int64_t npos, int width) {
+    int npairs = width / 2;
+    out->resize((size_t)npos * npairs);
+    for (int64_t p = 0; p < npos; ++p)
+      for (int j = 0; j < npairs; ++j) {
+        double ang = (double)p * std::pow((double)g.theta, -(double)(2 * j) / width);
+        (*out)[(size_t)p * npairs + j] = make_float2((float)std::cos(ang), (float)std::sin(ang));
+      }
+  };
+  fill(t, g.max_frames, dt);
+  fill(h, g.grid_h, dh);
+  fill(w, g.grid_w, dw);
+}
+
+void prof_begin(gca_cache* c, int kind, hipStream_t s, ProfRec* r) {
+  r->kind = -1;
+  if (c->prof_cap <= 0 || (int)c->prof.size() >= c->prof_cap || c->prof_pool.size() < 2) return;
+  r->kind = kind;
+  r->b = c->prof_pool.back();
+  c->prof_pool.pop_back();
+  r->a = c->prof_pool.back();
+  c->prof_pool.pop_back();
+  (void)hipEventRecord(r->a, s);
+}
+
+void prof_end(gca_cache* c, hipStream_t s, ProfRec* r) {
+  if (r->kind < 0) return;
+  (void)hipEventRecord(r->b, s);
+  c->prof.push_back(*r);
+}
+
+struct Prof {
+  gca_cache* c;
+  hipStream_t s;
+  ProfRec r;
+  Prof(gca_cache* c_, int kind, hipStream_t s_) : c(c_), s(s_) { prof_begin(c, kind, s, &r); }
+  ~Prof() { prof_end(c, s, &r); }
+};
+
+int do_select(gca_cache* c, hipStream_t s, gca::SelectStep* out) {
+  gca::SelectStep st = c->plan.select();
+  gca::SelectArgs a;
+  a.rec_pages = c->rec_pages;
+  a.traj_pages = c->traj_pages;
+  a.sel_page = c->sel_page;
+  a.sel_len = c->sel_len;
+  a.traj_len = st.traj_len;
+  a.ppf = c->g.ppf;
+  a.P = c->g.P;
+  a.last_len = c->g.last_len;
+  a.A = c->g.A;
+  a.Wr = c->g.Wr;
+  a.n_anchor = st.n_anchor;
+  a.win_first = st.win_first;
+  a.win_count = st.win_count;
+  a.n_traj_pages = st.n_traj_pages;
+  a.n_sel = st.n_sel;
+  {
+    Prof p(c, 2, s);
+    GCA_HIP(gca::launch_select(a, s), "select kernel launch");
+  }
+  c->sel_valid = true;
+  c->sel_n = st.n_sel;
+  c->sel_ctx = st.n_ctx;
+  if (out) *out = st;
+  return GCA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* gca_last_error(void) { return g_last_error.c_str(); }
+
+int gca_cache_create(const gca_config* cfg, gca_cache** out) {
+  if (!out) return GCA_ERR_INVALID_ARGUMENT;
+  *out = nullptr;
+  gca::Geometry g;
+  int rc = gca::make_geometry(cfg, &g);
+  if (rc) return rc;
+  gca_cache* c = new gca_cache(g);
+  auto fail = [&](hipError_t e, const char* what) {
+    int r = hip_fail(e, what);
+    free_all(c);
+    delete c;
+    return r;
+  };
+  hipError_t e;
+  if ((e = hipGetDevice(&c->device)) != hipSuccess) return fail(e, "hipGetDevice");
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, c->device) == hipSuccess &&
+      cus > 0)
+    c->num_cu = cus;
+  c->esize = g.dtype == GCA_BF16 ? 2 : 4;
+  size_t page_elems = (size_t)g.H * g.P * g.D;
+  size_t pool_bytes = (size_t)g.N * page_elems * c->esize;
+  size_t rows = (size_t)g.T * g.H;
+  if ((e = dmalloc(&c->kpool, pool_bytes)) != hipSuccess) return fail(e, "hipMalloc K pool");
+  if ((e = dmalloc(&c->vpool, pool_bytes)) != hipSuccess) return fail(e, "hipMalloc V pool");
+  if ((e = dmalloc(&c->ring, sizeof(int32_t) * g.N)) != hipSuccess) return fail(e, "hipMalloc ring");
+  if ((e = dmalloc(&c->rec_pages, sizeof(int32_t) * (size_t)(g.A + g.Wr) * g.ppf)) != hipSuccess)
+    return fail(e, "hipMalloc records");
+  if ((e = dmalloc(&c->traj_pages, sizeof(int32_t) * (size_t)g.traj_cap)) != hipSuccess)
+    return fail(e, "hipMalloc trajectory");
+  if ((e = dmalloc(&c->compact, sizeof(int32_t) * (size_t)g.C)) != hipSuccess)
+    return fail(e, "hipMalloc compact list");
+  if ((e = dmalloc(&c->sel_page, sizeof(int32_t) * (size_t)g.sel_cap)) != hipSuccess)
+    return fail(e, "hipMalloc gather list");
+  if ((e = dmalloc(&c->sel_len, sizeof(int32_t) * (size_t)g.sel_cap)) != hipSuccess)
+    return fail(e, "hipMalloc gather list");
+  if ((e = dmalloc(&c->o_part, sizeof(float) * rows * g.D * kMaxSplits)) != hipSuccess)
+    return fail(e, "hipMalloc split workspace");
+  if ((e = dmalloc(&c->lse_part, sizeof(float) * rows * kMaxSplits)) != hipSuccess)
+    return fail(e, "hipMalloc split workspace");
+  if ((e = hipMemset(c->kpool, 0, pool_bytes)) != hipSuccess) return fail(e, "hipMemset K pool");
+  if ((e = hipMemset(c->vpool, 0, pool_bytes)) != hipSuccess) return fail(e, "hipMemset V pool");
+  if (g.C) {
+    if ((e = hipMemcpy(c->compact, g.compact.data(), sizeof(int32_t) * g.C, hipMemcpyHostToDevice)) !=
+        hipSuccess)
+      return fail(e, "upload compact list");
+  }
+  std::vector<int32_t> ring(g.N);
+  for (int i = 0; i < g.N; ++i) ring[i] = g.ring_init.empty() ? i : g.ring_init[i];
+  if (!g.ring_init.empty()) {
+    if ((e = dmalloc(&c->ring_init, sizeof(int32_t) * g.N)) != hipSuccess) return fail(e, "hipMalloc ring order");
+    if ((e = hipMemcpy(c->ring_init, ring.data(), sizeof(int32_t) * g.N, hipMemcpyHostToDevice)) != hipSuccess)
+      return fail(e, "upload ring order");
+  }
+  if ((e = hipMemcpy(c->ring, ring.data(), sizeof(int32_t) * g.N, hipMemcpyHostToDevice)) != hipSuccess)
+    return fail(e, "upload ring");
+  if (g.rope) {
+    std::vector<float2> t, h, w;
+    int nt, nh, nw;
+    build_rope(g, &t, &h, &w, &nt, &nh, &nw);
+    if ((e = dmalloc(&c->rope_t, sizeof(float2) * t.size())) != hipSuccess) return fail(e, "hipMalloc rope");
+    if ((e = dmalloc(&c->rope_h, sizeof(float2) * h.size())) != hipSuccess) return fail(e, "hipMalloc rope");
+    if ((e = dmalloc(&c->rope_w, sizeof(float2) * w.size())) != hipSuccess) return fail(e, "hipMalloc rope");
+    if ((e = hipMemcpy(c->rope_t, t.data(), sizeof(float2) * t.size(), hipMemcpyHostToDevice)) != hipSuccess)
+      return fail(e, "upload rope");
+    if ((e = hipMemcpy(c->rope_h, h.data(), sizeof(float2) * h.size(), hipMemcpyHostToDevice)) != hipSuccess)
+      return fail(e, "upload rope");
+    if ((e = hipMemcpy(c->rope_w, w.data(), sizeof(float2) * w.size(), hipMemcpyHostToDevice)) != hipSuccess)
+      return fail(e, "upload rope");
+    c->tabs.t = c->rope_t;
+    c->tabs.h = c->rope_h;
+    c->tabs.w = c->rope_w;
+    c->tabs.nt = nt;
+    c->tabs.nh = nh;
+    c->tabs.nw = nw;
+    c->tabs.num_special = g.num_special;
+    c->tabs.grid_w = g.grid_w;
+  }
+  if ((e = hipDeviceSynchronize()) != hipSuccess) return fail(e, "create sync");
+  *out = c;
+  return GCA_OK;
+}
+
+int gca_cache_destroy(gca_cache* c) {
+  if (!c) return GCA_OK;
+  (void)hipSetDevice(c->device);
+  hipError_t e = hipDeviceSynchronize();
+  free_all(c);
+  delete c;
+  return e == hipSuccess ? GCA_OK : hip_fail(e, "destroy sync");
+}
+
+int gca_cache_reset(gca_cache* c, gca_stream_t stream) {
+  if (!c) return GCA_ERR_INVALID_ARGUMENT;
+  hipStream_t s = (hipStream_t)stream;
+  GCA_HIP(gca::launch_ring_init(c->ring, c->ring_init, c->g.N, s), "ring init launch");
+  c->plan.reset();
+  c->sel_valid = false;
+  return GCA_OK;
+}
+
+int gca_append_frame(gca_cache* c, int64_t frame_idx, const void* k, const void* v, uint32_t flags,
+                     gca_stream_t stream) {
+  if (!c || !aligned16(k) || !aligned16(v) || (flags & ~GCA_APPEND_TEMP))
+    return GCA_ERR_INVALID_ARGUMENT;
+  bool temp = flags & GCA_APPEND_TEMP;
+  gca::AppendStep st;
+  int rc = c->plan.check_append(frame_idx, temp, &st);
+  if (rc) return rc;
+  hipStream_t s = (hipStream_t)stream;
+  gca::AppendArgs a;
+  a.k = k;
+  a.v = v;
+  a.kpool = c->kpool;
+  a.vpool = c->vpool;
+  a.ring = c->ring;
+  a.rec_pages = c->rec_pages;
+  a.ring_pos = st.ring_pos % c->g.N;
+  a.frame = frame_idx;
+  a.N = c->g.N;
+  a.slot = st.slot;
+  a.ppf = c->g.ppf;
+  a.T = c->g.T;
+  a.H = c->g.H;
+  a.P = c->g.P;
+  a.rope = c->g.rope;
+  a.tabs = c->tabs;
+  {
+    Prof p(c, 0, s);
+    GCA_HIP(gca::launch_append(c->g.dtype, a, s), "append kernel launch");
+  }
+  c->plan.commit_append(st, temp);
+  c->sel_valid = false;
+  return GCA_OK;
+}
+
+int gca_evict_compact(gca_cache* c, gca_stream_t stream) {
+  if (!c) return GCA_ERR_INVALID_ARGUMENT;
+  std::vector<gca::EvictStep> steps;
+  int rc = c->plan.check_evict(&steps);
+  if (rc) return rc;
+  hipStream_t s = (hipStream_t)stream;
+  for (const gca::EvictStep& st : steps) {
+    gca::EvictArgs a;
+    a.kpool = c->kpool;
+    a.vpool = c->vpool;
+    a.ring = c->ring;
+    a.rec_pages = c->rec_pages;
+    a.traj_pages = c->traj_pages;
+    a.compact = c->compact;
+    a.traj_len = st.traj_len;
+    a.ring_head = st.ring_head % c->g.N;
+    a.ring_tail = st.ring_tail % c->g.N;
+    a.N = c->g.N;
+    a.slot = st.slot;
+    a.ppf = c->g.ppf;
+    a.n_traj_pages = st.n_traj_pages;
+    a.new_pages = st.new_pages;
+    a.C = c->g.C;
+    a.H = c->g.H;
+    a.P = c->g.P;
+    Prof p(c, 1, s);
+    GCA_HIP(gca::launch_evict(c->g.dtype, a, s), "evict kernel launch");
+  }
+  c->plan.commit_evict(steps);
+  if (!steps.empty()) c->sel_valid = false;
+  return GCA_OK;
+}
+
+int gca_select(gca_cache* c, gca_stream_t stream) {
+  if (!c) return GCA_ERR_INVALID_ARGUMENT;
+  if (c->plan.empty()) return GCA_ERR_SEQUENCE;
+  return do_select(c, (hipStream_t)stream, nullptr);
+}
+
+int gca_attend(gca_cache* c, int64_t frame_idx, const void* q, void* out, float* lse,
+               gca_stream_t stream) {
+  if (!c || !aligned16(q) || !aligned16(out) || (lse && ((uintptr_t)lse & 3)))
+    return GCA_ERR_INVALID_ARGUMENT;
+  int rc = c->plan.check_attend(frame_idx);
+  if (rc) return rc;
+  hipStream_t s = (hipStream_t)stream;
+  gca::SelectStep st;
+  rc = do_select(c, s, &st);
+  if (rc) return rc;
+  const gca::Geometry& g = c->g;
+  int ept = gca::kKeysPerTile / g.P;
+  int n_tiles = (st.n_sel + ept - 1) / ept;
+  int qpw = gca::queries_per_wg(g.dtype);
+  int qtiles = (g.T + qpw - 1) / qpw;
+  // split the context so that about two workgroups run per compute unit
+  int base = qtiles * g.H;
+  int S = (2 * c->num_cu + base - 1) / base;
+  S = std::min(S, kMaxSplits);
+  S = std::min(S, std::max(1, n_tiles / 2));
+  S = std::max(S, 1);
+  int tps = (n_tiles + S - 1) / S;
+  S = (n_tiles + tps - 1) / tps;
+  gca::AttnArgs a;
+  a.q = q;
+  a.kpool = c->kpool;
+  a.vpool = c->vpool;
+  a.sel_page = c->sel_page;
+  a.sel_len = c->sel_len;
+  a.o_part = c->o_part;
+  a.lse_part = c->lse_part;
+  a.out = out;
+  a.lse = lse;
+  a.frame = frame_idx;
+  a.sm_scale = g.scale;
+  a.c2 = (float)((double)g.scale * 1.4426950408889634);
+  a.Tq = g.T;
+  a.H = g.H;
+  a.P = g.P;
+  a.n_sel = st.n_sel;
+  a.n_tiles = n_tiles;
+  a.tiles_per_split = tps;
+  a.S = S;
+  a.n_qtiles = qtiles;
+  a.n_units = g.H * S;
+  a.out_bf16 = g.out_dtype == GCA_BF16;
+  a.rope = g.rope;
+  a.tabs = c->tabs;
+  {
+    Prof p(c, 3, s);
+    GCA_HIP(gca::launch_attn(g.dtype, a, s), "attention kernel launch");
+  }
+  if (S > 1) {
+    gca::MergeArgs m;
+    m.o_part = c->o_part;
+    m.lse_part = c->lse_part;
+    m.out = out;
+    m.lse = lse;
+    m.rows = g.T * g.H;
+    m.S = S;
+    m.out_bf16 = a.out_bf16;
+    Prof p(c, 4, s);
+    GCA_HIP(gca::launch_merge(m, s), "merge kernel launch");
+  }
+  return GCA_OK;
+}
+
+int gca_rollback_last_frame(gca_cache* c, int64_t frame_idx, gca_stream_t stream) {
+  (void)stream;
+  if (!c) return GCA_ERR_INVALID_ARGUMENT;
+  int rc = c->plan.check_rollback(frame_idx);
+  if (rc) return rc;
+  // The popped ring slots still hold the page ids: moving the head back
+  // returns them, and the frame's record slot is simply no longer live.
+  c->plan.commit_rollback();
+  c->sel_valid = false;
+  return GCA_OK;
+}
+
+int gca_rope3d(gca_cache* c, int64_t frame_idx, const void* x, void* y, gca_stream_t stream) {
+  if (!c || !aligned16(x) || !aligned16(y) || frame_idx < 0) return GCA_ERR_INVALID_ARGUMENT;
+  if (!c->g.rope) return GCA_ERR_UNSUPPORTED;
+  if (frame_idx >= c->g.max_frames) return GCA_ERR_CAPACITY;
+  hipStream_t s = (hipStream_t)stream;
+  gca::RopeArgs a;
+  a.x = x;
+  a.y = y;
+  a.frame = frame_idx;
+  a.T = c->g.T;
+  a.H = c->g.H;
+  a.tabs = c->tabs;
+  Prof p(c, 5, s);
+  GCA_HIP(gca::launch_rope(c->g.dtype, a, s), "rope kernel launch");
+  return GCA_OK;
+}
+
+int gca_query(const gca_cache* c, gca_info* out) {
+  if (!c || !out) return GCA_ERR_INVALID_ARGUMENT;
+  c->plan.info(out);
+  out->max_splits = kMaxSplits;
+  return GCA_OK;
+}
+
+int gca_export_state(gca_cache* c, gca_state_view* v, gca_stream_t stream) {
+  if (!c || !v) return GCA_ERR_INVALID_ARGUMENT;
+  GCA_HIP(hipStreamSynchronize((hipStream_t)stream), "export sync");
+  const gca::Geometry& g = c->g;
+  std::vector<int32_t> ring(g.N);
+  GCA_HIP(hipMemcpy(ring.data(), c->ring, sizeof(int32_t) * g.N, hipMemcpyDeviceToHost), "export ring");
+  int64_t head = c->plan.ring_head(), tail = c->plan.ring_tail();
+  v->n_free = (int32_t)(tail - head);
+  if (v->free_ring)
+    for (int64_t i = 0; i < tail - head; ++i) v->free_ring[i] = ring[(size_t)((head + i) % g.N)];
+  std::vector<int> slots;
+  std::vector<int64_t> frames;
+  c->plan.live_frames(&slots, &frames);
+  v->n_frames = (int32_t)slots.size();
+  std::vector<int32_t> rec((size_t)(g.A + g.Wr) * g.ppf);
+  GCA_HIP(hipMemcpy(rec.data(), c->rec_pages, sizeof(int32_t) * rec.size(), hipMemcpyDeviceToHost),
+          "export records");
+  for (size_t i = 0; i < slots.size(); ++i) {
+    if (v->frame_idx) v->frame_idx[i] = frames[i];
+    if (v->frame_pages)
+      std::memcpy(v->frame_pages + i * g.ppf, rec.data() + (size_t)slots[i] * g.ppf, sizeof(int32_t) * g.ppf);
+  }
+  gca_info inf;
+  c->plan.info(&inf);
+  v->n_traj_pages = inf.traj_pages;
+  v->traj_tokens = inf.traj_tokens;
+  if (v->traj_pages && inf.traj_pages)
+    GCA_HIP(hipMemcpy(v->traj_pages, c->traj_pages, sizeof(int32_t) * inf.traj_pages, hipMemcpyDeviceToHost),
+            "export trajectory");
+  v->n_sel = c->sel_valid ? c->sel_n : 0;
+  v->n_ctx = c->sel_valid ? c->sel_ctx : 0;
+  if (v->n_sel) {
+    if (v->sel_page)
+      GCA_HIP(hipMemcpy(v->sel_page, c->sel_page, sizeof(int32_t) * v->n_sel, hipMemcpyDeviceToHost),
+              "export gather list");
+    if (v->sel_len)
+      GCA_HIP(hipMemcpy(v->sel_len, c->sel_len, sizeof(int32_t) * v->n_sel, hipMemcpyDeviceToHost),
+              "export gather list");
+  }
+  return GCA_OK;
+}
+
+int gca_read_page(gca_cache* c, int32_t page, void* host_k, void* host_v, gca_stream_t stream) {
+  if (!c || page < 0 || page >= c->g.N || !host_k || !host_v) return GCA_ERR_INVALID_ARGUMENT;
+  GCA_HIP(hipStreamSynchronize((hipStream_t)stream), "read_page sync");
+  const gca::Geometry& g = c->g;
+  size_t n = (size_t)g.H * g.P * g.D;
+  size_t off = (size_t)page * n * c->esize;
+  GCA_HIP(hipMemcpy(host_k, (char*)c->kpool + off, n * c->esize, hipMemcpyDeviceToHost), "read K page");
+  std::vector<char> vt(n * c->esize);
+  GCA_HIP(hipMemcpy(vt.data(), (char*)c->vpool + off, n * c->esize, hipMemcpyDeviceToHost), "read V page");
+  // device V page is [H][D][P]; hand it out as [H][P][D]
+  char* dst = (char*)host_v;
+  for (int h = 0; h < g.H; ++h)
+    for (int d = 0; d < g.D; ++d)
+      for (int s = 0; s < g.P; ++s)
+        std::memcpy(dst + (((size_t)h * g.P + s) * g.D + d) * c->esize,
+                    vt.data() + (((size_t)h * g.D + d) * g.P + s) * c->esize, c->esize);
+  return GCA_OK;
+}
+
+int gca_profile_enable(gca_cache* c, int32_t capacity) {
+  if (!c || capacity < 0) return GCA_ERR_INVALID_ARGUMENT;
+  GCA_HIP(hipDeviceSynchronize(), "profile sync");
+  for (auto& r : c->prof) {
+    c->prof_pool.push_back(r.a);
+    c->prof_pool.push_back(r.b);
+  }
+  c->prof.clear();
+  c->prof_cap = capacity;
+  while ((int)c->prof_pool.size() < 2 * capacity) {
+    hipEvent_t e;
+    GCA_HIP(hipEventCreate(&e), "hipEventCreate");
+    c->prof_pool.push_back(e);
+  }
+  return GCA_OK;
+}
+
+int gca_profile_read(gca_cache* c, int32_t kind, double* total_ms, int32_t* count) {
+  if (!c || !total_ms || !count) return GCA_ERR_INVALID_ARGUMENT;
+  double sum = 0.0;
+  int n = 0;
+  std::vector<ProfRec> keep;
+  for (auto& r : c->prof) {
+    if (r.kind != kind) {
+      keep.push_back(r);
+      continue;
+    }
+    GCA_HIP(hipEventSynchronize(r.b), "profile event sync");
+    float ms = 0.f;
+    GCA_HIP(hipEventElapsedTime(&ms, r.a, r.b), "profile elapsed");
+    sum += ms;
+    n++;
+    c->prof_pool.push_back(r.a);
+    c->prof_pool.push_back(r.b);
+  }
+  c->prof.swap(keep);
+  *total_ms = sum;
+  *count = n;
+  return GCA_OK;
+}
+
+}  // extern "C"

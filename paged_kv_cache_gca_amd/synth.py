@@ -78,8 +78,8 @@ def round_bf16(x32: np.ndarray) -> np.ndarray:
     return out
 
 
-def to_dtype(x64: np.ndarray, dtype: str) -> np.ndarray:
-    x32 = x64.astype(np.float32)
+def to_dtype(x: np.ndarray, dtype: str) -> np.ndarray:
+    x32 = x.astype(np.float32)
     if dtype == "bf16":
         return round_bf16(x32)
     if dtype == "f32":
@@ -96,13 +96,22 @@ class FrameStream:
         self.n_base = n_base
         self.drift_sigma = drift_sigma
         self._drift_cache: dict[int, tuple[np.ndarray, np.ndarray]] = {0: (np.zeros((H, D)), np.zeros((H, D)))}
+        self._base_cache: dict[tuple[int, int], np.ndarray] = {}
 
     def slot(self, frame: int) -> int:
         return frame if self.n_base is None else frame % self.n_base
 
     def base(self, frame: int, tensor: int) -> np.ndarray:
+        """float32 draws (before any bf16 rounding) of one frame tensor [T, H, D]."""
+        key = (self.slot(frame), tensor)
+        hit = self._base_cache.get(key)
+        if hit is not None:
+            return hit
         n = self.T * self.H * self.D
-        return normals(self.seed, self.slot(frame), tensor, n).reshape(self.T, self.H, self.D)
+        x = normals(self.seed, key[0], tensor, n).reshape(self.T, self.H, self.D).astype(np.float32)
+        if self.n_base is not None:  # cycled streams: at most 3 * n_base tensors
+            self._base_cache[key] = x
+        return x
 
     def drift(self, frame: int) -> tuple[np.ndarray, np.ndarray]:
         """(mu_K, mu_V) of shape [H, D] after `frame` steps of the random walk."""
@@ -128,8 +137,8 @@ class FrameStream:
         if self.drift_sigma:
             mk, mv = self.drift(frame)
             # the offset is added in float32 to the float32 base draw, then rounded
-            k32 = k.astype(np.float32) + mk.astype(np.float32)[None]
-            v32 = v.astype(np.float32) + mv.astype(np.float32)[None]
+            k32 = k + mk.astype(np.float32)[None]
+            v32 = v + mv.astype(np.float32)[None]
             if self.dtype == "bf16":
                 return round_bf16(k32), round_bf16(v32)
             return k32, v32

@@ -1,0 +1,284 @@
+"""GPU parity of the HIP path against the CPU oracle, through the C ABI.
+
+Bar: page tables, ring and gather lists bit-exact; V pages bit-exact and K'
+pages within one unit in the last place (the library rotates in float32 from
+float32 tables, the oracle in float64); attention max abs error <= 1e-5 for the
+float32 stream and <= 2e-2 for bf16 streams.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from paged_kv_cache_gca_amd import workloads as WL
+from paged_kv_cache_gca_amd.synth import FrameStream
+from tests.gpu_pair import Pair, dev, gca, oracle_cfg, stream_of
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-5, "bf16": 2e-2}
+LSE_TOL = {"f32": 1e-5, "bf16": 2e-3}
+
+
+def _cmp_attention(pair, f, rows=None):
+    q, out, lse = pair.attend_gpu(f)
+    T = pair.w.T
+    rows = np.arange(T, dtype=np.int32) if rows is None else np.asarray(rows, dtype=np.int32)
+    o_ref, lse_ref = pair.orc.attend(f, q, rows=rows)
+    o = out.float().cpu().numpy()[rows].astype(np.float64)
+    l = lse.cpu().numpy()[rows].astype(np.float64)
+    err = float(np.abs(o - o_ref).max())
+    lerr = float(np.abs(l - lse_ref).max())
+    tol = TOL[pair.w.dtype]
+    if pair.cfg.out_dtype == "bf16":
+        tol = max(tol, 2e-2)
+    assert np.isfinite(o).all()
+    assert err <= tol, (f, err)
+    assert lerr <= LSE_TOL[pair.w.dtype], (f, lerr)
+    return err, lerr
+
+
+def test_tiny_f32_stream_full_parity():
+    """6 frames x 64 tokens, 2 heads, fp32: every step, every row, every page."""
+    w = WL.TINY_F32
+    p = Pair(w)
+    errs = []
+    for f in range(w.n_frames):
+        p.step(f)
+        gs = p.check_state()
+        mis, tot = p.check_pages(gs, k_ulps=0)
+        assert mis == 0
+        errs.append(_cmp_attention(p, f))
+    print("tiny f32 max err", max(e[0] for e in errs))
+
+
+SMALL = dict(T=300, H=4, D=64, dtype="bf16", n_frames=12, A=1, W=3, C=5, rope=1,
+             num_special=3, grid_h=9, grid_w=33, seed=21)
+
+
+@pytest.mark.parametrize("P,interval,out_dtype", [
+    (16, 1, "f32"), (32, 2, "f32"), (64, 3, "bf16"), (16, 2, "bf16"),
+])
+def test_small_bf16_stream_parity(P, interval, out_dtype):
+    """Ragged query tile (300 = 256 + 44), ragged frame tail, TEMP frames."""
+    w = WL.Workload(f"small_P{P}", P=P, keyframe_interval=interval, **SMALL)
+    p = Pair(w, out_dtype=out_dtype)
+    kmis = ktot = 0
+    for f in range(w.n_frames):
+        key = p.step(f)
+        gs = p.check_state()
+        m, t = p.check_pages(gs)
+        kmis += m
+        ktot += t
+        _cmp_attention(p, f)
+        if not key:
+            p.rollback(f)
+            p.check_state()
+    assert kmis <= 1e-3 * ktot, (kmis, ktot)
+
+
+def test_ring_window_no_anchor_no_trajectory():
+    w = WL.Workload("small_ring", T=300, H=2, D=64, P=64, dtype="bf16", n_frames=10, A=0, W=3, C=0,
+                    rope=1, num_special=3, grid_h=9, grid_w=33, seed=22)
+    p = Pair(w)
+    for f in range(w.n_frames):
+        p.step(f)
+        gs = p.check_state()
+        assert len(gs["traj_pages"]) == 0
+        _cmp_attention(p, f)
+
+
+def test_keep_every_token_and_window_never_full():
+    # C = T keeps whole frames in the trajectory; W larger than the stream never evicts
+    for C, W in [(64, 1), (0, 50)]:
+        w = WL.Workload(f"edge_C{C}_W{W}", T=64, H=2, D=64, P=16, dtype="f32", n_frames=5, A=1, W=W,
+                        C=C, rope=0, num_special=0, grid_h=8, grid_w=8, seed=23)
+        p = Pair(w)
+        for f in range(w.n_frames):
+            p.step(f)
+            p.check_state()
+            _cmp_attention(p, f)
+
+
+def _rows(T, n=48, seed=0):
+    rng = np.random.default_rng(seed)
+    fixed = [0, 1, 2, 3, 4, 5, 36, 37, 255, 256, 511, 512, 767, 768, 1000, T - 1]
+    extra = rng.choice(T, n - len(fixed), replace=False).tolist()
+    return np.unique(np.array([r for r in fixed + extra if r < T], dtype=np.int32))
+
+
+def test_frame1004_w16_p16_stream_sampled():
+    """The 518x378 frame shape (1004 tokens, 16 heads), 64 frames, P=16, full stream."""
+    w = WL.FRAME1004_W16
+    p = Pair(w)
+    rows = _rows(w.T)
+    for f in range(w.n_frames):
+        p.step(f)
+        p.check_state()
+        if f in (0, 1, 16, 17, 40, 63):
+            _cmp_attention(p, f, rows)
+
+
+@pytest.mark.parametrize("w,last,samples", [
+    (WL.STREAM1000_W64, 100, (64, 65, 100)),
+    (WL.STREAM10K_KF4, 150, (132, 148, 149, 150)),
+])
+def test_long_stream_prefix_sampled(w, last, samples):
+    """Full-size frames and pools; attention sampled on a prefix of the stream."""
+    p = Pair(w)
+    rows = _rows(w.T, seed=1)
+    for f in range(last + 1):
+        key = p.step(f)
+        if f % 10 == 0 or f in samples:
+            p.check_state()
+        if f in samples:
+            _cmp_attention(p, f, rows)
+        if not key:
+            p.rollback(f)
+
+
+def test_ring20k_tail_sampled():
+    """Strict 12-frame window at the end of the 20,000-frame stream (t near 19,999)."""
+    w = WL.RING20K_W12
+    p = Pair(w)
+    rows = _rows(w.T, seed=2)
+    for f in range(19976, 20000):
+        p.step(f)
+        p.check_state()
+    _cmp_attention(p, 19999, rows)
+
+
+@pytest.mark.parametrize("w", [WL.FRAME1004_W16, WL.STREAM1000_W64, WL.STREAM10K_KF4, WL.RING20K_W12],
+                         ids=lambda w: w.name)
+def test_fullsize_bookkeeping_every_step(w):
+    """Ring, page tables and gather list bit-exact at every step of the whole stream."""
+    p = Pair(w, data=False)
+    for f in range(w.n_frames):
+        key = p.step(f)
+        p.check_state(with_select=True)
+        if not key:
+            p.rollback(f)
+            if f % 50 == 1:
+                p.check_state(with_select=False)
+
+
+def test_rope_standalone_matches_oracle():
+    w = WL.FRAME1004_W16
+    g = gca()
+    c = g.Cache(g.Config.from_workload(w, max_frames=20000))
+    fs = FrameStream(99, w.T, w.H, w.D, "bf16")
+    for f in (0, 1, 777, 19999):
+        x = fs.q(f)
+        y = torch.empty((w.T, w.H, w.D), dtype=torch.bfloat16, device="cuda")
+        assert c.rope3d(f, dev(x, "bf16"), y) == 0
+        got = y.float().cpu().numpy().astype(np.float64)
+        ref64 = oracle.rope(oracle_cfg(w, max_frames=20000), f, x)
+        m, e = np.frexp(ref64)
+        ref = np.ldexp(np.rint(m * 256.0), e - 8)
+        diff = got != ref
+        assert (np.abs(got - ref)[diff] <= np.abs(ref[diff]) * 2.0 ** -7).all()
+        assert diff.mean() < 1e-3, diff.mean()
+
+
+def test_fused_rope_in_append_is_bitwise_standalone():
+    w = WL.FRAME1004_W16
+    g = gca()
+    cfg = g.Config.from_workload(w)
+    c = g.Cache(cfg)
+    fs = stream_of(w)
+    k, v = fs.kv(5)
+    kd, vd = dev(k, "bf16"), dev(v, "bf16")
+    assert c.append_frame(5, kd, vd) == 0
+    y = torch.empty_like(kd)
+    assert c.rope3d(5, kd, y) == 0
+    st = c.export_state()
+    pages = st["frame_pages"][0]
+    yh = y.float().cpu().numpy()
+    for i, pg in enumerate(pages):
+        gk, gv = c.read_page(int(pg))
+        n = min(w.P, w.T - i * w.P)
+        np.testing.assert_array_equal(gk[:, :n], yh[i * w.P:i * w.P + n].transpose(1, 0, 2))
+        np.testing.assert_array_equal(gv[:, :n], v[i * w.P:i * w.P + n].transpose(1, 0, 2))
+        assert (gk[:, n:] == 0).all() and (gv[:, n:] == 0).all()
+
+
+def _run_outputs(w, frames, **kw):
+    p = Pair(w, **kw)
+    outs = []
+    for f in frames:
+        key = p.step(f)
+        _, out, lse = p.attend_gpu(f)
+        outs.append((out.cpu().clone(), lse.cpu().clone()))
+        if not key:
+            p.rollback(f)
+    return p, outs
+
+
+def test_page_relabelling_and_determinism_bitwise():
+    """Paged == contiguous: physical page ids do not change a single output bit."""
+    w = WL.Workload("relabel", T=300, H=4, D=64, P=16, dtype="bf16", n_frames=9, A=1, W=3, C=5,
+                    rope=1, num_special=3, grid_h=9, grid_w=33, keyframe_interval=2, seed=31)
+    base, o0 = _run_outputs(w, range(9))
+    _, o1 = _run_outputs(w, range(9))
+    perm = np.random.default_rng(5).permutation(base.gpu.info.num_pages).tolist()
+    rel, o2 = _run_outputs(w, range(9), ring_init=perm)
+    for (a, la), (b, lb), (c, lc) in zip(o0, o1, o2):
+        assert torch.equal(a, b) and torch.equal(la, lb)
+        assert torch.equal(a, c) and torch.equal(la, lc)
+    rel.check_state()
+
+
+def test_closed_form_special_cases():
+    """K = 0: O = mean of the context's V; V = 1: O = 1."""
+    g = gca()
+    w = WL.Workload("special", T=300, H=4, D=64, P=16, dtype="bf16", n_frames=6, A=1, W=2, C=5,
+                    rope=1, num_special=3, grid_h=9, grid_w=33, seed=41)
+    cfg = g.Config.from_workload(w)
+    c0, c1 = g.Cache(cfg), g.Cache(cfg)
+    o = oracle.OracleCache(oracle_cfg(w))
+    fs = stream_of(w)
+    zeros = torch.zeros((w.T, w.H, w.D), dtype=torch.bfloat16, device="cuda")
+    ones = torch.ones_like(zeros)
+    for f in range(w.n_frames):
+        k, v = fs.kv(f)
+        assert c0.append_frame(f, zeros, dev(v, "bf16")) == 0 and c0.evict_compact() == 0
+        assert c1.append_frame(f, dev(k, "bf16"), ones) == 0 and c1.evict_compact() == 0
+        assert o.append(f, np.zeros_like(k), v) == 0 and o.evict() == 0
+        q = dev(fs.q(f), "bf16")
+        out0 = torch.empty((w.T, w.H, w.D), dtype=torch.float32, device="cuda")
+        out1 = torch.empty_like(out0)
+        assert c0.attend(f, q, out0) == 0 and c1.attend(f, q, out1) == 0
+        _, vc, _, _ = o.context()
+        mean = vc.astype(np.float64).mean(0)
+        np.testing.assert_allclose(out0.cpu().numpy(), np.broadcast_to(mean, out0.shape), atol=1e-5)
+        np.testing.assert_allclose(out1.cpu().numpy(), 1.0, atol=1e-6)
+
+
+def test_device_error_paths_change_nothing():
+    g = gca()
+    w = WL.TINY_F32
+    p = Pair(w)
+    for f in range(4):
+        p.step(f)
+    before = p.gpu.export_state()
+    k = torch.zeros((w.T, w.H, w.D), dtype=torch.float32, device="cuda")
+    assert p.gpu.append_frame(3, k, k) == g.GCA_ERR_SEQUENCE
+    assert p.gpu.append_frame(6, k, k) == g.GCA_ERR_CAPACITY
+    assert p.gpu.attend(2, k, k) == g.GCA_ERR_SEQUENCE
+    assert p.gpu.rollback_last_frame(3) == g.GCA_ERR_SEQUENCE
+    bad = k.view(-1)[1:].view(-1)  # misaligned by 4 bytes
+    assert p.gpu.append_frame(4, bad, k) == g.GCA_ERR_INVALID_ARGUMENT
+    after = p.gpu.export_state()
+    for key in ("free", "frame_idx", "frame_pages", "traj_pages"):
+        np.testing.assert_array_equal(before[key], after[key])
+    # out of pages: a cache with room for two frames
+    q = g.Cache(g.Config.from_workload(w, num_pages=9))
+    assert q.append_frame(0, k, k) == 0 and q.append_frame(1, k, k) == 0
+    assert q.append_frame(2, k, k) == g.GCA_ERR_OUT_OF_PAGES
+    # reset restores the initial ring
+    assert p.gpu.reset() == 0
+    p.orc.reset()
+    p.step(0)
+    p.check_state()

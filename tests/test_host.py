@@ -1,0 +1,149 @@
+"""Host-side tests (no GPU): the C ABI library loads and exports every symbol
+declared in include/gca.h, and the host planner (the occupancy state machine
+the cache runs before enqueuing kernels) validates configs and call sequences
+and reports the same occupancy as the oracle's allocator model."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import oracle
+from paged_kv_cache_gca_amd import workloads as WL
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gca.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(gca_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    from paged_kv_cache_gca_amd import gca
+    names = _declared()
+    assert len(names) >= 24
+    lib = ctypes.CDLL(gca.LIB_PATH)
+    missing = [n for n in names if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+def test_status_strings():
+    from paged_kv_cache_gca_amd import gca
+    assert gca.status_string(0) == "ok"
+    for code in range(-6, 0):
+        assert gca.status_string(code) != "unknown status"
+
+
+def cfg_of(w, **kw):
+    from paged_kv_cache_gca_amd import gca
+    return gca.Config.from_workload(w, **kw)
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("head_dim", 128, -6),
+    ("head_dim", 0, -1),
+    ("page_size", 24, -1),
+    ("page_size", 128, -6),
+    ("window_frames", 0, -1),
+    ("num_compact", 70, -1),
+    ("num_anchor_frames", -1, -1),
+    ("sm_scale", -0.125, -1),
+    ("max_frames", 0, -1),
+    ("compact_idx", [3, 3], -1),
+    ("compact_idx", [64], -1),
+])
+def test_plan_rejects_bad_configs(field, value, code):
+    from paged_kv_cache_gca_amd import gca
+    c = cfg_of(WL.TINY_F32)
+    setattr(c, field, value)
+    if field == "compact_idx":
+        c.num_compact = len(value)
+    with pytest.raises(gca.GCAError) as ei:
+        gca.Plan(c)
+    assert ei.value.code == code
+
+
+def test_plan_rejects_rope_grid_mismatch_and_bad_ring():
+    from paged_kv_cache_gca_amd import gca
+    c = cfg_of(WL.FRAME1004_W16, grid_w=36)
+    with pytest.raises(gca.GCAError):
+        gca.Plan(c)
+    c = cfg_of(WL.TINY_F32, ring_init=list(range(16)) + [0])
+    with pytest.raises(gca.GCAError):
+        gca.Plan(c)
+
+
+def test_plan_sequence_errors():
+    from paged_kv_cache_gca_amd import gca
+    p = gca.Plan(cfg_of(WL.TINY_F32))
+    assert p.attend(0) == gca.GCA_ERR_SEQUENCE          # nothing appended
+    assert p.append(-1) == gca.GCA_ERR_INVALID_ARGUMENT
+    assert p.append(0) == 0
+    assert p.append(0) == gca.GCA_ERR_SEQUENCE          # not increasing
+    assert p.attend(1) == gca.GCA_ERR_SEQUENCE          # not the last frame
+    assert p.attend(0) == 0
+    assert p.rollback(0) == gca.GCA_ERR_SEQUENCE        # not a TEMP frame
+    assert p.append(1) == 0 and p.append(2) == 0 and p.append(3) == 0
+    assert p.append(4) == gca.GCA_ERR_SEQUENCE          # W+1 window frames: evict first
+    assert p.evict() == 0
+    assert p.append(4, temp=True) == 0
+    assert p.evict() == gca.GCA_ERR_SEQUENCE            # TEMP pending
+    assert p.append(5) == gca.GCA_ERR_SEQUENCE
+    before = p.query()
+    assert p.rollback(4) == 0
+    assert p.append(6) == gca.GCA_ERR_CAPACITY          # max_frames = 6
+    info = p.query()
+    assert info.temp_pending == 0 and before.temp_pending == 1
+    assert info.free_pages == before.free_pages + info.pages_per_frame
+
+
+def test_plan_out_of_pages_changes_nothing():
+    from paged_kv_cache_gca_amd import gca
+    p = gca.Plan(cfg_of(WL.TINY_F32, num_pages=9))
+    assert p.append(0) == 0 and p.append(1) == 0
+    before = p.query()
+    assert p.append(2) == gca.GCA_ERR_OUT_OF_PAGES
+    after = p.query()
+    for f, _ in gca.gca_info._fields_:
+        assert getattr(before, f) == getattr(after, f)
+
+
+def test_default_num_pages_matches_oracle_rule():
+    from paged_kv_cache_gca_amd import gca
+    for w in WL.ALL:
+        p = gca.Plan(cfg_of(w))
+        assert p.query().num_pages == oracle.default_num_pages(
+            oracle.OracleConfig(T=w.T, H=w.H, D=w.D, P=w.P, A=w.A, W=w.W, C=w.C,
+                                max_frames=w.n_frames))
+
+
+@pytest.mark.parametrize("w", WL.ALL, ids=lambda w: w.name)
+def test_plan_occupancy_matches_oracle_every_step(w):
+    from paged_kv_cache_gca_amd import gca
+    p = gca.Plan(cfg_of(w))
+    o = oracle.OracleCache(oracle.OracleConfig(T=w.T, H=w.H, D=w.D, P=w.P, A=w.A, W=w.W, C=w.C,
+                                               num_special=w.num_special, max_frames=w.n_frames))
+    n = min(w.n_frames, 3000)
+    for f in range(n):
+        key = w.is_keyframe(f)
+        assert p.append(f, temp=not key) == 0
+        assert o.append(f, None, None, temp=not key) == 0
+        if key:
+            assert p.evict() == 0 and o.evict() == 0
+        assert p.attend(f) == 0
+        info = p.query()
+        assert info.n_ctx == o.n_ctx()
+        if f % 97 == 0 or f == n - 1:
+            page, ln, n_ctx = o.select()
+            st = o.state()
+            assert info.n_sel == len(page)
+            assert info.free_pages == len(st["free"])
+            assert info.traj_pages == len(st["traj_pages"])
+            assert info.traj_tokens == st["traj_len"]
+        if not key:
+            assert p.rollback(f) == 0 and o.rollback(f) == 0
