@@ -322,21 +322,104 @@ __device__ inline void load_q(const AttnArgs& a, int qbase, int h, int l32, int 
   }
 }
 
-template <typename T>
+// Per-thread share of staging one 64-key tile into LDS.  Thread t copies the
+// 16-byte chunks t and t + 256 (and so on) of the K tile (64 keys x 64 dims,
+// token-major) and of the V^T tile (64 dims x 64 keys).
+template <typename T, int P>
+struct TileLoader {
+  static constexpr int EPC = 16 / sizeof(T);           // elements per 16-byte chunk
+  static constexpr int EPT = kKeysPerTile / P;         // gather entries per tile
+  static constexpr int CPRK = kHeadDim / EPC;          // chunks per K row
+  static constexpr int CPRV = kKeysPerTile / EPC;      // chunks per V^T row
+  static constexpr int NC = kKeysPerTile * CPRK / 256; // chunks per thread (K and V alike)
+  static constexpr int KP = kHeadDim + EPC;            // LDS pitches (one 16-byte pad)
+  static constexpr int VP = kKeysPerTile + EPC;
+
+  int k_ei[NC], k_off[NC], k_lds[NC];  // entry in tile, element offset in page, LDS offset
+  int v_ei, v_off[NC], v_lds[NC], v_slot0;
+  int pg_k[NC], pg_v, len_v;           // page ids / valid length of the next tile
+  uint4 kr[NC], vr[NC];
+  int len_me;                          // thread < EPT: valid length of its entry
+  int dlen_v, dlen_me;                 // lengths of the tile held in kr / vr
+
+  __device__ void init(int tid, int h, int H) {
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
+      int c = tid + 256 * i;
+      int r = c / CPRK, part = c % CPRK;
+      k_ei[i] = r / P;
+      k_off[i] = ((h * P) + (r % P)) * kHeadDim + part * EPC;  // + page * H * P * D
+      k_lds[i] = r * KP + part * EPC;
+      int d = c / CPRV, kc = c % CPRV;
+      int k0 = kc * EPC;
+      v_off[i] = (h * kHeadDim + d) * P + (k0 % P);
+      v_lds[i] = d * VP + k0;
+      if (i == 0) {
+        v_ei = k0 / P;
+        v_slot0 = k0 % P;
+      }
+    }
+  }
+  // page ids (and V length) of tile `tile`; -1 past the end of the list
+  __device__ void fetch_pages(const AttnArgs& a, int tile, int tid) {
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
+      int e = tile * EPT + k_ei[i];
+      pg_k[i] = e < a.n_sel ? a.sel_page[e] : -1;
+    }
+    int e = tile * EPT + v_ei;
+    pg_v = e < a.n_sel ? a.sel_page[e] : -1;
+    len_v = e < a.n_sel ? a.sel_len[e] : 0;
+    len_me = 0;
+    if (tid < EPT) {
+      int e2 = tile * EPT + tid;
+      len_me = e2 < a.n_sel ? a.sel_len[e2] : 0;
+    }
+  }
+  __device__ void fetch_data(const T* kpool, const T* vpool, int H) {
+    const size_t page_elems = (size_t)H * P * kHeadDim;
+    dlen_v = len_v;
+    dlen_me = len_me;
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
+      kr[i] = make_uint4(0, 0, 0, 0);
+      if (pg_k[i] >= 0) kr[i] = *(const uint4*)(kpool + (size_t)pg_k[i] * page_elems + k_off[i]);
+      vr[i] = make_uint4(0, 0, 0, 0);
+      if (pg_v >= 0) vr[i] = *(const uint4*)(vpool + (size_t)pg_v * page_elems + v_off[i]);
+    }
+  }
+  __device__ void store(T* lk, T* lv, int* llen, int tid) {
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
+      *(uint4*)(lk + k_lds[i]) = kr[i];
+      Vec16<T> v;
+      v.u = vr[i];
+      if (v_slot0 + EPC > dlen_v) {  // keys past the entry's length contribute nothing
+#pragma unroll
+        for (int j = 0; j < EPC; ++j)
+          if (v_slot0 + j >= dlen_v) v.e[j] = from_f<T>(0.f);
+      }
+      *(uint4*)(lv + v_lds[i]) = v.u;
+    }
+    if (tid < EPT) llen[tid] = dlen_me;
+  }
+};
+
+template <typename T, int P>
 __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
   using M = Mfma<T>;
   using Frag = typename M::Frag;
+  using L = TileLoader<T, P>;
   constexpr int NQB = M::NQB;
   constexpr int KPL = M::KPL;
   constexpr int NDC = kHeadDim / (2 * KPL);  // MFMAs along the head dim
   constexpr int NCH = 16 / KPL;              // P^T operands per 32-key block
-  constexpr int EPC = 16 / sizeof(T);
-  constexpr int KP = kHeadDim + EPC;         // K tile row pitch
-  constexpr int VP = kKeysPerTile + EPC;     // V^T tile row pitch
+  constexpr int EPT = L::EPT;
   constexpr int QPW = NQB * 32;              // queries per wave
-  __shared__ __attribute__((aligned(16))) T lk[kKeysPerTile * KP];
-  __shared__ __attribute__((aligned(16))) T lv[kHeadDim * VP];
-  __shared__ int llen[kKeysPerTile / 16];
+  // double-buffered tiles
+  __shared__ __attribute__((aligned(16))) T lk[2][kKeysPerTile * L::KP];
+  __shared__ __attribute__((aligned(16))) T lv[2][kHeadDim * L::VP];
+  __shared__ __attribute__((aligned(16))) int llen[2][4];
 
   // workgroup -> (head, split, q tile): the q tiles of one (head, split) are
   // consecutive on one XCD (dispatch is round-robin over XCDs), so they share
@@ -349,15 +432,25 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
   const int h = unit / a.S, split = unit % a.S;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hi = lane >> 5;
-  const int ept = kKeysPerTile / a.P;
   const int t0 = split * a.tiles_per_split;
   const int t1 = min(a.n_tiles, t0 + a.tiles_per_split);
   const int qbase = (qt * kWaves + wave) * QPW;
   const T* kpool = (const T*)a.kpool;
   const T* vpool = (const T*)a.vpool;
 
+  L ld;
+  ld.init(tid, h, a.H);
+  if (t0 < t1) {
+    ld.fetch_pages(a, t0, tid);
+    ld.fetch_data(kpool, vpool, a.H);
+    ld.fetch_pages(a, t0 + 1, tid);
+  }
+
   Frag qf[NQB][NDC];
   load_q(a, qbase, h, l32, hi, qf);
+
+  if (t0 < t1) ld.store(lk[t0 & 1], lv[t0 & 1], llen[t0 & 1], tid);
+  __syncthreads();
 
   floatx16 o[2][NQB];
 #pragma unroll
@@ -374,73 +467,50 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
   }
   const Frag ones = M::ones();
   const float c2 = a.c2;
+  // The running max is only raised when a tile's max exceeds it by more than
+  // 2^8 in exp2 units; below that, exp2 stays <= 256, exact enough in fp32/bf16.
+  const float thr = 8.0f / c2;
 
   for (int tile = t0; tile < t1; ++tile) {
-    __syncthreads();  // previous tile fully consumed
-    if (tid < ept) {
-      int e = tile * ept + tid;
-      llen[tid] = e < a.n_sel ? a.sel_len[e] : 0;
+    const int buf = tile & 1;
+    const bool more = tile + 1 < t1;
+    if (more) {
+      ld.fetch_data(kpool, vpool, a.H);           // tile + 1, lands during this tile's math
+      ld.fetch_pages(a, tile + 2, tid);           // page ids two tiles ahead
     }
-    constexpr int CPRK = kHeadDim / EPC;
-    for (int c = tid; c < kKeysPerTile * CPRK; c += 256) {
-      int r = c / CPRK, part = c - r * CPRK;
-      int e = tile * ept + r / a.P;
-      int slot = r % a.P;
-      uint4 val = make_uint4(0, 0, 0, 0);
-      if (e < a.n_sel) {
-        int pg = a.sel_page[e];
-        val = *(const uint4*)(kpool + (((size_t)pg * a.H + h) * a.P + slot) * kHeadDim + part * EPC);
-      }
-      *(uint4*)(lk + r * KP + part * EPC) = val;
-    }
-    constexpr int CPRV = kKeysPerTile / EPC;
-    for (int c = tid; c < kHeadDim * CPRV; c += 256) {
-      int d = c / CPRV, kc = c - d * CPRV;
-      int k0 = kc * EPC;
-      int e = tile * ept + k0 / a.P;
-      int slot0 = k0 % a.P;
-      Vec16<T> val;
-      val.u = make_uint4(0, 0, 0, 0);
-      if (e < a.n_sel) {
-        int pg = a.sel_page[e], len = a.sel_len[e];
-        val.u = *(const uint4*)(vpool + (((size_t)pg * a.H + h) * kHeadDim + d) * a.P + slot0);
-        if (slot0 + EPC > len) {
-#pragma unroll
-          for (int i = 0; i < EPC; ++i)
-            if (slot0 + i >= len) val.e[i] = from_f<T>(0.f);
-        }
-      }
-      *(uint4*)(lv + d * VP + k0) = val.u;
-    }
-    __syncthreads();
+    const T* ck = lk[buf];
+    const T* cv = lv[buf];
 
     // S^T = K Q^T: s[kb][qb] holds keys kb*32 + 8*(r/4) + 4*hi + r%4 of query column l32
     floatx16 s[2][NQB];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int qb = 0; qb < NQB; ++qb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[kb][qb][r] = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
       for (int dc = 0; dc < NDC; ++dc) {
-        Frag kf = read_k(lk, KP, kb * 32 + l32, dc, hi);
+        Frag kf = read_k(ck, L::KP, kb * 32 + l32, dc, hi);
 #pragma unroll
-        for (int qb = 0; qb < NQB; ++qb) s[kb][qb] = M::mma(kf, qf[qb][dc], s[kb][qb]);
+        for (int qb = 0; qb < NQB; ++qb) {
+          if (dc == 0) {
+            floatx16 z;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) z[r] = 0.f;
+            s[kb][qb] = M::mma(kf, qf[qb][dc], z);
+          } else {
+            s[kb][qb] = M::mma(kf, qf[qb][dc], s[kb][qb]);
+          }
+        }
       }
 
     bool full = true;
-    for (int i = 0; i < ept; ++i) full = full && (llen[i] == a.P);
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) full = full && (llen[buf][i] == P);
     if (!full) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           int key = kb * 32 + (r >> 2) * 8 + hi * 4 + (r & 3);
-          bool ok = (key % a.P) < llen[key / a.P];
-          if (!ok) {
+          if ((key % P) >= llen[buf][key / P]) {
 #pragma unroll
             for (int qb = 0; qb < NQB; ++qb) s[kb][qb][r] = -INFINITY;
           }
@@ -457,10 +527,16 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[1][qb][r]);
       mx = fmaxf(mx, __shfl_xor(mx, 32));
-      float mn = fmaxf(m[qb], mx);
-      float alpha = __builtin_amdgcn_exp2f((m[qb] - mn) * c2);
-      m[qb] = mn;
-      float mc = mn * c2;
+      bool raise = mx > m[qb] + thr;
+      if (__any(raise)) {
+        float mn = raise ? mx : m[qb];
+        float alpha = __builtin_amdgcn_exp2f((m[qb] - mn) * c2);
+        m[qb] = mn;
+        o[0][qb] *= alpha;
+        o[1][qb] *= alpha;
+        l[qb] *= alpha;
+      }
+      float mc = m[qb] * c2;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
@@ -469,9 +545,6 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
 #pragma unroll
         for (int ch = 0; ch < NCH; ++ch) pf[kb][ch][qb] = pack_p(s[kb][qb], ch, T());
       }
-      o[0][qb] *= alpha;
-      o[1][qb] *= alpha;
-      l[qb] *= alpha;
     }
 
     // O^T += V^T P^T
@@ -481,7 +554,7 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
       for (int ch = 0; ch < NCH; ++ch)
 #pragma unroll
         for (int db = 0; db < 2; ++db) {
-          Frag vf = read_v(lv, VP, db * 32 + l32, kb, ch, hi);
+          Frag vf = read_v(cv, L::VP, db * 32 + l32, kb, ch, hi);
 #pragma unroll
           for (int qb = 0; qb < NQB; ++qb) o[db][qb] = M::mma(vf, pf[kb][ch][qb], o[db][qb]);
         }
@@ -497,6 +570,10 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
         for (int ch = 0; ch < NCH; ++ch) lt = M::mma(ones, pf[kb][ch][qb], lt);
       l[qb] += lt[0];
     }
+
+    // the other buffer was last read in the previous tile, before its barrier
+    if (more) ld.store(lk[buf ^ 1], lv[buf ^ 1], llen[buf ^ 1], tid);
+    __syncthreads();
   }
 
   // epilogue: O^T accumulators hold dims db*32 + 8*(r/4) + 4*hi + r%4
@@ -535,23 +612,44 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
   }
 }
 
+// Split merge: 16 threads per (token, head) row, 4 dims each; all partial
+// loads of a thread are independent and issued together.
+constexpr int kMaxSplitsDev = 16;
+
 __global__ __launch_bounds__(256) void k_merge(MergeArgs a) {
-  int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-  int d = threadIdx.x & 63;
+  int row = blockIdx.x * 16 + (threadIdx.x >> 4);
+  int d = (threadIdx.x & 15) * 4;
   if (row >= a.rows) return;
+  float ls[kMaxSplitsDev];
   float mx = -INFINITY;
-  for (int s = 0; s < a.S; ++s) mx = fmaxf(mx, a.lse_part[(size_t)s * a.rows + row]);
-  float sum = 0.f, acc = 0.f;
-  for (int s = 0; s < a.S; ++s) {
-    float ls = a.lse_part[(size_t)s * a.rows + row];
-    if (ls == -INFINITY) continue;
-    float w = __expf(ls - mx);
-    sum += w;
-    acc = __builtin_fmaf(w, a.o_part[((size_t)s * a.rows + row) * kHeadDim + d], acc);
+#pragma unroll
+  for (int s = 0; s < kMaxSplitsDev; ++s) {
+    ls[s] = s < a.S ? a.lse_part[(size_t)s * a.rows + row] : -INFINITY;
+    mx = fmaxf(mx, ls[s]);
   }
-  float v = acc / sum;
-  if (a.out_bf16) ((bf16*)a.out)[(size_t)row * kHeadDim + d] = (bf16)v;
-  else ((float*)a.out)[(size_t)row * kHeadDim + d] = v;
+  floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+  float sum = 0.f;
+#pragma unroll
+  for (int s = 0; s < kMaxSplitsDev; ++s) {
+    if (s < a.S && ls[s] != -INFINITY) {
+      float w = __expf(ls[s] - mx);
+      floatx4 v = *(const floatx4*)(a.o_part + ((size_t)s * a.rows + row) * kHeadDim + d);
+      sum += w;
+      acc[0] = __builtin_fmaf(w, v[0], acc[0]);
+      acc[1] = __builtin_fmaf(w, v[1], acc[1]);
+      acc[2] = __builtin_fmaf(w, v[2], acc[2]);
+      acc[3] = __builtin_fmaf(w, v[3], acc[3]);
+    }
+  }
+  float inv = 1.f / sum;
+  acc[0] *= inv; acc[1] *= inv; acc[2] *= inv; acc[3] *= inv;
+  if (a.out_bf16) {
+    bf16x4 w;
+    w[0] = (bf16)acc[0]; w[1] = (bf16)acc[1]; w[2] = (bf16)acc[2]; w[3] = (bf16)acc[3];
+    *(bf16x4*)((bf16*)a.out + (size_t)row * kHeadDim + d) = w;
+  } else {
+    *(floatx4*)((float*)a.out + (size_t)row * kHeadDim + d) = acc;
+  }
   if (d == 0 && a.lse) a.lse[row] = mx + __logf(sum);
 }
 
@@ -580,13 +678,21 @@ hipError_t launch_select(const SelectArgs& a, hipStream_t s) {
 hipError_t launch_attn(int dtype, const AttnArgs& a, hipStream_t s) {
   int groups = (a.n_units + kNumXcd - 1) / kNumXcd;
   dim3 grid(groups * kNumXcd * a.n_qtiles);
-  if (dtype) hipLaunchKernelGGL(k_attn<bf16>, grid, dim3(256), 0, s, a);
-  else hipLaunchKernelGGL(k_attn<float>, grid, dim3(256), 0, s, a);
+  switch (dtype * 100 + a.P) {
+    case 116: hipLaunchKernelGGL((k_attn<bf16, 16>), grid, dim3(256), 0, s, a); break;
+    case 132: hipLaunchKernelGGL((k_attn<bf16, 32>), grid, dim3(256), 0, s, a); break;
+    case 164: hipLaunchKernelGGL((k_attn<bf16, 64>), grid, dim3(256), 0, s, a); break;
+    case 16: hipLaunchKernelGGL((k_attn<float, 16>), grid, dim3(256), 0, s, a); break;
+    case 32: hipLaunchKernelGGL((k_attn<float, 32>), grid, dim3(256), 0, s, a); break;
+    case 64: hipLaunchKernelGGL((k_attn<float, 64>), grid, dim3(256), 0, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
 hipError_t launch_merge(const MergeArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(k_merge, dim3((a.rows + 3) / 4), dim3(256), 0, s, a);
+  if (a.S > kMaxSplitsDev) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_merge, dim3((a.rows + 15) / 16), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
