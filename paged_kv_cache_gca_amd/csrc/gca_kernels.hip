@@ -324,7 +324,8 @@ __device__ inline void load_q(const AttnArgs& a, int qbase, int h, int l32, int 
 
 // Per-thread share of staging one 64-key tile into LDS.  Thread t copies the
 // 16-byte chunks t and t + 256 (and so on) of the K tile (64 keys x 64 dims,
-// token-major) and of the V^T tile (64 dims x 64 keys).
+// token-major) and of the V^T tile (64 dims x 64 keys).  Chunks of gather
+// entries past the end of the list read page 0 instead; their keys are masked.
 template <typename T, int P>
 struct TileLoader {
   static constexpr int EPC = 16 / sizeof(T);           // elements per 16-byte chunk
@@ -334,41 +335,29 @@ struct TileLoader {
   static constexpr int NC = kKeysPerTile * CPRK / 256; // chunks per thread (K and V alike)
   static constexpr int KP = kHeadDim + EPC;            // LDS pitches (one 16-byte pad)
   static constexpr int VP = kKeysPerTile + EPC;
+  static constexpr int TILE_ELEMS = kKeysPerTile * KP + kHeadDim * VP;
 
-  int k_ei[NC], k_off[NC], k_lds[NC];  // entry in tile, element offset in page, LDS offset
-  int v_ei, v_off[NC], v_lds[NC], v_slot0;
-  int pg_k[NC], pg_v, len_v;           // page ids / valid length of the next tile
+  // chunk i of thread t: K row r = c / CPRK, part c % CPRK; V^T row d = c / CPRV,
+  // keys (c % CPRV) * EPC.. with c = t + 256 i.  c % CPRV does not depend on i.
+  __device__ static int k_row(int tid, int i) { return (tid + 256 * i) / CPRK; }
+  __device__ static int k_part(int tid) { return tid % CPRK; }
+  __device__ static int v_row(int tid, int i) { return (tid + 256 * i) / CPRV; }
+  __device__ static int v_key0(int tid) { return (tid % CPRV) * EPC; }
+
+  int pg_k[NC], pg_v, len_v;  // page ids / valid length of the next tile
   uint4 kr[NC], vr[NC];
-  int len_me;                          // thread < EPT: valid length of its entry
-  int dlen_v, dlen_me;                 // lengths of the tile held in kr / vr
+  int len_me;                 // thread < EPT: valid length of its entry
+  int dlen_v, dlen_me;        // lengths of the tile held in kr / vr
 
-  __device__ void init(int tid, int h, int H) {
-#pragma unroll
-    for (int i = 0; i < NC; ++i) {
-      int c = tid + 256 * i;
-      int r = c / CPRK, part = c % CPRK;
-      k_ei[i] = r / P;
-      k_off[i] = ((h * P) + (r % P)) * kHeadDim + part * EPC;  // + page * H * P * D
-      k_lds[i] = r * KP + part * EPC;
-      int d = c / CPRV, kc = c % CPRV;
-      int k0 = kc * EPC;
-      v_off[i] = (h * kHeadDim + d) * P + (k0 % P);
-      v_lds[i] = d * VP + k0;
-      if (i == 0) {
-        v_ei = k0 / P;
-        v_slot0 = k0 % P;
-      }
-    }
-  }
-  // page ids (and V length) of tile `tile`; -1 past the end of the list
+  // page ids (and lengths) of tile `tile`; entries past the list read page 0
   __device__ void fetch_pages(const AttnArgs& a, int tile, int tid) {
 #pragma unroll
     for (int i = 0; i < NC; ++i) {
-      int e = tile * EPT + k_ei[i];
-      pg_k[i] = e < a.n_sel ? a.sel_page[e] : -1;
+      int e = tile * EPT + k_row(tid, i) / P;
+      pg_k[i] = e < a.n_sel ? a.sel_page[e] : 0;
     }
-    int e = tile * EPT + v_ei;
-    pg_v = e < a.n_sel ? a.sel_page[e] : -1;
+    int e = tile * EPT + v_key0(tid) / P;
+    pg_v = e < a.n_sel ? a.sel_page[e] : 0;
     len_v = e < a.n_sel ? a.sel_len[e] : 0;
     len_me = 0;
     if (tid < EPT) {
@@ -376,34 +365,60 @@ struct TileLoader {
       len_me = e2 < a.n_sel ? a.sel_len[e2] : 0;
     }
   }
-  __device__ void fetch_data(const T* kpool, const T* vpool, int H) {
+  __device__ void fetch_data(const T* kpool, const T* vpool, int h, int H, int tid) {
     const size_t page_elems = (size_t)H * P * kHeadDim;
     dlen_v = len_v;
     dlen_me = len_me;
 #pragma unroll
     for (int i = 0; i < NC; ++i) {
-      kr[i] = make_uint4(0, 0, 0, 0);
-      if (pg_k[i] >= 0) kr[i] = *(const uint4*)(kpool + (size_t)pg_k[i] * page_elems + k_off[i]);
-      vr[i] = make_uint4(0, 0, 0, 0);
-      if (pg_v >= 0) vr[i] = *(const uint4*)(vpool + (size_t)pg_v * page_elems + v_off[i]);
+      int r = k_row(tid, i);
+      kr[i] = *(const uint4*)(kpool + (size_t)pg_k[i] * page_elems +
+                              ((h * P) + (r % P)) * kHeadDim + k_part(tid) * EPC);
+      vr[i] = *(const uint4*)(vpool + (size_t)pg_v * page_elems +
+                              (h * kHeadDim + v_row(tid, i)) * P + (v_key0(tid) % P));
     }
   }
-  __device__ void store(T* lk, T* lv, int* llen, int tid) {
+  __device__ void store(T* tileb, int* llen, int tid) {
+    const int slot0 = v_key0(tid) % P;
 #pragma unroll
     for (int i = 0; i < NC; ++i) {
-      *(uint4*)(lk + k_lds[i]) = kr[i];
+      *(uint4*)(tileb + k_row(tid, i) * KP + k_part(tid) * EPC) = kr[i];
       Vec16<T> v;
       v.u = vr[i];
-      if (v_slot0 + EPC > dlen_v) {  // keys past the entry's length contribute nothing
+      if (slot0 + EPC > dlen_v) {  // keys past the entry's length contribute nothing
 #pragma unroll
         for (int j = 0; j < EPC; ++j)
-          if (v_slot0 + j >= dlen_v) v.e[j] = from_f<T>(0.f);
+          if (slot0 + j >= dlen_v) v.e[j] = from_f<T>(0.f);
       }
-      *(uint4*)(lv + v_lds[i]) = v.u;
+      *(uint4*)(tileb + kKeysPerTile * KP + v_row(tid, i) * VP + v_key0(tid)) = v.u;
     }
     if (tid < EPT) llen[tid] = dlen_me;
   }
 };
+
+// Row sums of P from the same rounded values the P.V product uses (this
+// lane's keys only; the lane pair l, l ^ 32 covers the whole tile).
+__device__ inline float rowsum_add(float l, bf16x8 p) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  bf16x2 one;
+  one[0] = (bf16)1.0f;
+  one[1] = (bf16)1.0f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    bf16x2 pr;
+    pr[0] = p[2 * i];
+    pr[1] = p[2 * i + 1];
+    l = __builtin_amdgcn_fdot2_f32_bf16(pr, one, l, false);
+  }
+  return l;
+}
+__device__ inline float rowsum_add(float l, float p) { return l + p; }
+
+// max over the two 32-lane halves of the wave
+__device__ inline float half_swap_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
 
 template <typename T, int P>
 __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
@@ -416,9 +431,7 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
   constexpr int NCH = 16 / KPL;              // P^T operands per 32-key block
   constexpr int EPT = L::EPT;
   constexpr int QPW = NQB * 32;              // queries per wave
-  // double-buffered tiles
-  __shared__ __attribute__((aligned(16))) T lk[2][kKeysPerTile * L::KP];
-  __shared__ __attribute__((aligned(16))) T lv[2][kHeadDim * L::VP];
+  __shared__ __attribute__((aligned(16))) T lt[2][L::TILE_ELEMS];  // double-buffered tiles
   __shared__ __attribute__((aligned(16))) int llen[2][4];
 
   // workgroup -> (head, split, q tile): the q tiles of one (head, split) are
@@ -439,17 +452,14 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
   const T* vpool = (const T*)a.vpool;
 
   L ld;
-  ld.init(tid, h, a.H);
   if (t0 < t1) {
     ld.fetch_pages(a, t0, tid);
-    ld.fetch_data(kpool, vpool, a.H);
+    ld.fetch_data(kpool, vpool, h, a.H, tid);
     ld.fetch_pages(a, t0 + 1, tid);
   }
-
   Frag qf[NQB][NDC];
   load_q(a, qbase, h, l32, hi, qf);
-
-  if (t0 < t1) ld.store(lk[t0 & 1], lv[t0 & 1], llen[t0 & 1], tid);
+  if (t0 < t1) ld.store(lt[t0 & 1], llen[t0 & 1], tid);
   __syncthreads();
 
   floatx16 o[2][NQB];
@@ -465,7 +475,6 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
     m[qb] = -INFINITY;
     l[qb] = 0.f;
   }
-  const Frag ones = M::ones();
   const float c2 = a.c2;
   // The running max is only raised when a tile's max exceeds it by more than
   // 2^8 in exp2 units; below that, exp2 stays <= 256, exact enough in fp32/bf16.
@@ -475,18 +484,18 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
     const int buf = tile & 1;
     const bool more = tile + 1 < t1;
     if (more) {
-      ld.fetch_data(kpool, vpool, a.H);           // tile + 1, lands during this tile's math
+      ld.fetch_data(kpool, vpool, h, a.H, tid);   // tile + 1, lands during this tile's math
       ld.fetch_pages(a, tile + 2, tid);           // page ids two tiles ahead
     }
-    const T* ck = lk[buf];
-    const T* cv = lv[buf];
+    const T* ck = lt[buf];
+    const T* cv = lt[buf] + kKeysPerTile * L::KP;
 
     // S^T = K Q^T: s[kb][qb] holds keys kb*32 + 8*(r/4) + 4*hi + r%4 of query column l32
     floatx16 s[2][NQB];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int dc = 0; dc < NDC; ++dc)
 #pragma unroll
-      for (int dc = 0; dc < NDC; ++dc) {
+      for (int kb = 0; kb < 2; ++kb) {
         Frag kf = read_k(ck, L::KP, kb * 32 + l32, dc, hi);
 #pragma unroll
         for (int qb = 0; qb < NQB; ++qb) {
@@ -501,41 +510,57 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
         }
       }
 
-    bool full = true;
-#pragma unroll
-    for (int i = 0; i < EPT; ++i) full = full && (llen[buf][i] == P);
+    // keys past a gather entry's valid length (partial pages) are masked
+    int4 lens = *(const int4*)llen[buf];
+    bool full = lens.x == P;
+    if (EPT > 1) full = full && lens.y == P;
+    if (EPT > 2) full = full && lens.z == P && lens.w == P;
     if (!full) {
+      int lv[4] = {lens.x, lens.y, lens.z, lens.w};
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           int key = kb * 32 + (r >> 2) * 8 + hi * 4 + (r & 3);
-          if ((key % P) >= llen[buf][key / P]) {
+          if ((key % P) >= lv[key / P]) {
 #pragma unroll
             for (int qb = 0; qb < NQB; ++qb) s[kb][qb][r] = -INFINITY;
           }
         }
     }
 
-    // online softmax, one query column per lane; P packed to MFMA operands
-    Frag pf[2][NCH][NQB];
+    // running max per query column (one column per lane); raise it only when
+    // the tile exceeds it by the threshold
+    bool raise[NQB];
+    float mx[NQB];
+    bool any = false;
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb) {
-      float mx = s[0][qb][0];
+      float x = s[0][qb][0];
 #pragma unroll
-      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[0][qb][r]);
+      for (int r = 1; r < 16; ++r) x = fmaxf(x, s[0][qb][r]);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[1][qb][r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      bool raise = mx > m[qb] + thr;
-      if (__any(raise)) {
-        float mn = raise ? mx : m[qb];
+      for (int r = 0; r < 16; ++r) x = fmaxf(x, s[1][qb][r]);
+      mx[qb] = half_swap_max(x);
+      raise[qb] = mx[qb] > m[qb] + thr;
+      any = any || raise[qb];
+    }
+    if (__any(any)) {
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) {
+        float mn = raise[qb] ? mx[qb] : m[qb];
         float alpha = __builtin_amdgcn_exp2f((m[qb] - mn) * c2);
         m[qb] = mn;
         o[0][qb] *= alpha;
         o[1][qb] *= alpha;
         l[qb] *= alpha;
       }
+    }
+
+    // P = exp2(S - m) rounded to the MFMA operand type; row sums of the same P
+    Frag pf[2][NCH][NQB];
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) {
       float mc = m[qb] * c2;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
@@ -543,7 +568,10 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
         for (int r = 0; r < 16; ++r)
           s[kb][qb][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][qb][r], c2, -mc));
 #pragma unroll
-        for (int ch = 0; ch < NCH; ++ch) pf[kb][ch][qb] = pack_p(s[kb][qb], ch, T());
+        for (int ch = 0; ch < NCH; ++ch) {
+          pf[kb][ch][qb] = pack_p(s[kb][qb], ch, T());
+          l[qb] = rowsum_add(l[qb], pf[kb][ch][qb]);
+        }
       }
     }
 
@@ -558,23 +586,16 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
 #pragma unroll
           for (int qb = 0; qb < NQB; ++qb) o[db][qb] = M::mma(vf, pf[kb][ch][qb], o[db][qb]);
         }
-    // row sums of the same rounded P, via an all-ones A operand
-#pragma unroll
-    for (int qb = 0; qb < NQB; ++qb) {
-      floatx16 lt;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) lt[r] = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int ch = 0; ch < NCH; ++ch) lt = M::mma(ones, pf[kb][ch][qb], lt);
-      l[qb] += lt[0];
-    }
 
     // the other buffer was last read in the previous tile, before its barrier
-    if (more) ld.store(lk[buf ^ 1], lv[buf ^ 1], llen[buf ^ 1], tid);
+    if (more) ld.store(lt[buf ^ 1], llen[buf ^ 1], tid);
     __syncthreads();
   }
+
+  // Each lane summed P over its own half of the keys (rows 4*hi + ...); both
+  // halves share the running max, so the two partial sums simply add.
+#pragma unroll
+  for (int qb = 0; qb < NQB; ++qb) l[qb] += __shfl_xor(l[qb], 32);
 
   // epilogue: O^T accumulators hold dims db*32 + 8*(r/4) + 4*hi + r%4
 #pragma unroll
