@@ -37,7 +37,21 @@ def parse():
     ap.add_argument("--workload", default="bf16_T1004_H16_P16_W16_64f")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=64)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 256 MiB device-to-device copy (counter calibration)")
     return ap.parse_args()
+
+
+def calibrate_copy():
+    """A plain copy of known size: read 256 MiB, write 256 MiB, five times."""
+    import torch
+    n = 256 << 20
+    x = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    for _ in range(5):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 5}))
 
 
 def kernel_hash() -> str:
@@ -180,6 +194,9 @@ def run_cpu_baseline(w, rows_per_frame):
 
 def main():
     args = parse()
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
         sys.exit(2)

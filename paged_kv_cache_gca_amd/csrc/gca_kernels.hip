@@ -433,6 +433,11 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
   constexpr int QPW = NQB * 32;              // queries per wave
   __shared__ __attribute__((aligned(16))) T lt[2][L::TILE_ELEMS];  // double-buffered tiles
   __shared__ __attribute__((aligned(16))) int llen[2][4];
+  // bf16: each wave's rotated query fragments wait in LDS in operand order
+  // [qb][dc][lane] (conflict-free 16-byte reads), freeing 32 VGPRs so LDS
+  // operand reads can be issued well ahead of their MFMAs.
+  constexpr bool QLDS = sizeof(T) == 2;
+  __shared__ __attribute__((aligned(16))) Frag lq[QLDS ? kWaves * NQB * NDC * 64 : 1];
 
   // workgroup -> (head, split, q tile): the q tiles of one (head, split) are
   // consecutive on one XCD (dispatch is round-robin over XCDs), so they share
@@ -457,8 +462,18 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
     ld.fetch_data(kpool, vpool, h, a.H, tid);
     ld.fetch_pages(a, t0 + 1, tid);
   }
-  Frag qf[NQB][NDC];
-  load_q(a, qbase, h, l32, hi, qf);
+  Frag qf[QLDS ? 1 : NQB][QLDS ? 1 : NDC];
+  Frag* mq = lq + wave * (NQB * NDC * 64);
+  if constexpr (QLDS) {
+    Frag qtmp[NQB][NDC];
+    load_q(a, qbase, h, l32, hi, qtmp);
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb)
+#pragma unroll
+      for (int dc = 0; dc < NDC; ++dc) mq[(qb * NDC + dc) * 64 + lane] = qtmp[qb][dc];
+  } else {
+    load_q(a, qbase, h, l32, hi, qf);
+  }
   if (t0 < t1) ld.store(lt[t0 & 1], llen[t0 & 1], tid);
   __syncthreads();
 
@@ -493,7 +508,13 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
     // S^T = K Q^T: s[kb][qb] holds keys kb*32 + 8*(r/4) + 4*hi + r%4 of query column l32
     floatx16 s[2][NQB];
 #pragma unroll
-    for (int dc = 0; dc < NDC; ++dc)
+    for (int dc = 0; dc < NDC; ++dc) {
+      Frag qv[NQB];
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) {
+        if constexpr (QLDS) qv[qb] = mq[(qb * NDC + dc) * 64 + lane];
+        else qv[qb] = qf[qb][dc];
+      }
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         Frag kf = read_k(ck, L::KP, kb * 32 + l32, dc, hi);
@@ -503,12 +524,13 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
             floatx16 z;
 #pragma unroll
             for (int r = 0; r < 16; ++r) z[r] = 0.f;
-            s[kb][qb] = M::mma(kf, qf[qb][dc], z);
+            s[kb][qb] = M::mma(kf, qv[qb], z);
           } else {
-            s[kb][qb] = M::mma(kf, qf[qb][dc], s[kb][qb]);
+            s[kb][qb] = M::mma(kf, qv[qb], s[kb][qb]);
           }
         }
       }
+    }
 
     // keys past a gather entry's valid length (partial pages) are masked
     int4 lens = *(const int4*)llen[buf];
