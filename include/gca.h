@@ -204,7 +204,8 @@ int gca_export_state(gca_cache* cache, gca_state_view* view, gca_stream_t stream
 int gca_read_page(gca_cache* cache, int32_t page, void* host_k, void* host_v, gca_stream_t stream);
 
 /* Kernel timing with HIP events recorded around every launch on its stream.
- * kind: 0 append, 1 evict, 2 select, 3 attention, 4 split merge, 5 rope.
+ * kind: 0 append, 1 evict, 2 selection (inside gca_attend it also rotates
+ * the queries), 3 attention, 4 split merge, 5 rope.
  * gca_profile_enable(cache, capacity) starts recording up to `capacity`
  * launches (0 stops); gca_profile_read synchronises and returns the summed
  * milliseconds and launch count of one kind, then forgets them. */

@@ -58,7 +58,7 @@ struct SelectArgs {
 };
 
 struct AttnArgs {
-  const void* q;       // raw [Tq][H][D]
+  const void* q;       // rotated [Tq][H][D]
   const void* kpool;   // [N][H][P][D]
   const void* vpool;   // [N][H][D][P]
   const int32_t* sel_page;
@@ -72,8 +72,6 @@ struct AttnArgs {
   float c2;            // sm_scale * log2(e)
   int Tq, H, P, n_sel, n_tiles, tiles_per_split, S, n_qtiles, n_units;
   int out_bf16;
-  int rope;
-  RopeTabs tabs;
 };
 
 struct MergeArgs {
@@ -98,6 +96,8 @@ struct RopeArgs {
 hipError_t launch_append(int dtype, const AppendArgs& a, hipStream_t s);
 hipError_t launch_evict(int dtype, const EvictArgs& a, hipStream_t s);
 hipError_t launch_select(const SelectArgs& a, hipStream_t s);
+// gather list and query rotation (into ra.y) in one launch
+hipError_t launch_prepare(int dtype, const SelectArgs& sa, const RopeArgs& ra, hipStream_t s);
 hipError_t launch_attn(int dtype, const AttnArgs& a, hipStream_t s);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t s);
 hipError_t launch_rope(int dtype, const RopeArgs& a, hipStream_t s);

@@ -198,6 +198,43 @@ __global__ __launch_bounds__(256) void k_select(SelectArgs a) {
   a.sel_len[e] = len;
 }
 
+// One launch per attention call: blocks [0, sel_blocks) build the gather
+// list, the remaining blocks rotate the frame's queries into a workspace.
+template <typename T>
+__global__ __launch_bounds__(256) void k_prepare(SelectArgs sa, RopeArgs ra, int sel_blocks) {
+  if ((int)blockIdx.x < sel_blocks) {
+    int e = blockIdx.x * 256 + threadIdx.x;
+    if (e >= sa.n_sel) return;
+    int nf = (sa.n_anchor + sa.win_count) * sa.ppf;
+    int page, len;
+    if (e < nf) {
+      int f = e / sa.ppf, i = e - f * sa.ppf;
+      int slot = f < sa.n_anchor ? f : sa.A + (sa.win_first + (f - sa.n_anchor)) % sa.Wr;
+      page = sa.rec_pages[slot * sa.ppf + i];
+      len = (i == sa.ppf - 1) ? sa.last_len : sa.P;
+    } else {
+      int ti = e - nf;
+      page = sa.traj_pages[ti];
+      int64_t rem = sa.traj_len - (int64_t)ti * sa.P;
+      len = rem < sa.P ? (int)rem : sa.P;
+    }
+    sa.sel_page[e] = page;
+    sa.sel_len[e] = len;
+    return;
+  }
+  constexpr int EPC = 16 / sizeof(T);
+  constexpr int CPR = kHeadDim / EPC;
+  size_t c = (size_t)(blockIdx.x - sel_blocks) * 256 + threadIdx.x;
+  size_t total = (size_t)ra.T * ra.H * CPR;
+  if (c >= total) return;
+  int part = (int)(c % CPR);
+  int tok = (int)(c / CPR / ra.H);
+  Vec16<T> v;
+  v.u = ((const uint4*)ra.x)[c];
+  rotate_chunk<T>(v, ra.tabs, ra.frame, tok, part * EPC / 2);
+  ((uint4*)ra.y)[c] = v.u;
+}
+
 __global__ void k_ring_init(int32_t* ring, const int32_t* init, int N) {
   int i = blockIdx.x * 256 + threadIdx.x;
   if (i < N) ring[i] = init ? init[i] : i;
@@ -276,8 +313,8 @@ __device__ inline bf16x8 pack_p(const floatx16& s, int ch, bf16) {
 }
 __device__ inline float pack_p(const floatx16& s, int ch, float) { return s[ch]; }
 
-// Rotated queries as B operands: lane holds query qb*32 + l32, dims
-// [dc*2*KPL + hi*KPL, +KPL).
+// Queries (already rotated) as B operands: lane holds query qb*32 + l32,
+// dims [dc*2*KPL + hi*KPL, +KPL).
 __device__ inline void load_q(const AttnArgs& a, int qbase, int h, int l32, int hi, bf16x8 (&qf)[2][4]) {
   const bf16* Q = (const bf16*)a.q;
 #pragma unroll
@@ -287,11 +324,7 @@ __device__ inline void load_q(const AttnArgs& a, int qbase, int h, int l32, int 
     for (int dc = 0; dc < 4; ++dc) {
       Vec16<bf16> v;
       v.u = make_uint4(0, 0, 0, 0);
-      int d0 = dc * 16 + hi * 8;
-      if (q < a.Tq) {
-        v.u = *(const uint4*)(Q + ((size_t)q * a.H + h) * kHeadDim + d0);
-        if (a.rope) rotate_chunk<bf16>(v, a.tabs, a.frame, q, d0 / 2);
-      }
+      if (q < a.Tq) v.u = *(const uint4*)(Q + ((size_t)q * a.H + h) * kHeadDim + dc * 16 + hi * 8);
       bf16x8 f;
 #pragma unroll
       for (int i = 0; i < 8; ++i) f[i] = v.e[i];
@@ -301,31 +334,12 @@ __device__ inline void load_q(const AttnArgs& a, int qbase, int h, int l32, int 
 }
 __device__ inline void load_q(const AttnArgs& a, int qbase, int h, int l32, int hi, float (&qf)[1][32]) {
   const float* Q = (const float*)a.q;
+  int q = qbase + l32;
 #pragma unroll
-  for (int qb = 0; qb < 1; ++qb) {
-    int q = qbase + qb * 32 + l32;
-#pragma unroll
-    for (int dc = 0; dc < 32; ++dc) {
-      float x = 0.f;
-      if (q < a.Tq) {
-        float2 p = *(const float2*)(Q + ((size_t)q * a.H + h) * kHeadDim + dc * 2);
-        if (a.rope) {
-          float y0, y1;
-          rotate(p.x, p.y, rope_cs(a.tabs, a.frame, q, dc), y0, y1);
-          p.x = y0;
-          p.y = y1;
-        }
-        x = hi ? p.y : p.x;
-      }
-      qf[qb][dc] = x;
-    }
-  }
+  for (int dc = 0; dc < 32; ++dc)
+    qf[0][dc] = q < a.Tq ? Q[((size_t)q * a.H + h) * kHeadDim + dc * 2 + hi] : 0.f;
 }
 
-// Per-thread share of staging one 64-key tile into LDS.  Thread t copies the
-// 16-byte chunks t and t + 256 (and so on) of the K tile (64 keys x 64 dims,
-// token-major) and of the V^T tile (64 dims x 64 keys).  Chunks of gather
-// entries past the end of the list read page 0 instead; their keys are masked.
 template <typename T, int P>
 struct TileLoader {
   static constexpr int EPC = 16 / sizeof(T);           // elements per 16-byte chunk
@@ -715,6 +729,16 @@ hipError_t launch_evict(int dtype, const EvictArgs& a, hipStream_t s) {
 hipError_t launch_select(const SelectArgs& a, hipStream_t s) {
   if (a.n_sel <= 0) return hipSuccess;
   hipLaunchKernelGGL(k_select, dim3((a.n_sel + 255) / 256), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_prepare(int dtype, const SelectArgs& sa, const RopeArgs& ra, hipStream_t s) {
+  int sel_blocks = (sa.n_sel + 255) / 256;
+  size_t chunks = (size_t)ra.T * ra.H * (dtype ? 8 : 16);
+  int rope_blocks = (int)((chunks + 255) / 256);
+  dim3 grid(sel_blocks + rope_blocks);
+  if (dtype) hipLaunchKernelGGL(k_prepare<bf16>, grid, dim3(256), 0, s, sa, ra, sel_blocks);
+  else hipLaunchKernelGGL(k_prepare<float>, grid, dim3(256), 0, s, sa, ra, sel_blocks);
   return hipGetLastError();
 }
 

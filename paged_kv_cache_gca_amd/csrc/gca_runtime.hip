@@ -65,6 +65,7 @@ struct gca_cache {
   gca::RopeTabs tabs{};
   float* o_part = nullptr;
   float* lse_part = nullptr;
+  void* qrot = nullptr;  // rotated queries of the current attention call
   bool sel_valid = false;
   int sel_n = 0;
   int64_t sel_ctx = 0;
@@ -81,7 +82,7 @@ namespace {
 void free_all(gca_cache* c) {
   void* ptrs[] = {c->kpool, c->vpool, c->ring, c->ring_init, c->rec_pages, c->traj_pages,
                   c->compact, c->sel_page, c->sel_len, c->rope_t, c->rope_h, c->rope_w,
-                  c->o_part, c->lse_part};
+                  c->o_part, c->lse_part, c->qrot};
   for (void* p : ptrs)
     if (p) (void)hipFree(p);
   for (auto& r : c->prof) {
@@ -143,6 +144,26 @@ struct Prof {
   Prof(gca_cache* c_, int kind, hipStream_t s_) : c(c_), s(s_) { prof_begin(c, kind, s, &r); }
   ~Prof() { prof_end(c, s, &r); }
 };
+
+gca::SelectArgs select_args(gca_cache* c, const gca::SelectStep& st) {
+  gca::SelectArgs a;
+  a.rec_pages = c->rec_pages;
+  a.traj_pages = c->traj_pages;
+  a.sel_page = c->sel_page;
+  a.sel_len = c->sel_len;
+  a.traj_len = st.traj_len;
+  a.ppf = c->g.ppf;
+  a.P = c->g.P;
+  a.last_len = c->g.last_len;
+  a.A = c->g.A;
+  a.Wr = c->g.Wr;
+  a.n_anchor = st.n_anchor;
+  a.win_first = st.win_first;
+  a.win_count = st.win_count;
+  a.n_traj_pages = st.n_traj_pages;
+  a.n_sel = st.n_sel;
+  return a;
+}
 
 int do_select(gca_cache* c, hipStream_t s, gca::SelectStep* out) {
   gca::SelectStep st = c->plan.select();
@@ -219,6 +240,8 @@ int gca_cache_create(const gca_config* cfg, gca_cache** out) {
     return fail(e, "hipMalloc split workspace");
   if ((e = dmalloc(&c->lse_part, sizeof(float) * rows * kMaxSplits)) != hipSuccess)
     return fail(e, "hipMalloc split workspace");
+  if (g.rope && (e = dmalloc(&c->qrot, rows * g.D * c->esize)) != hipSuccess)
+    return fail(e, "hipMalloc query workspace");
   if ((e = hipMemset(c->kpool, 0, pool_bytes)) != hipSuccess) return fail(e, "hipMemset K pool");
   if ((e = hipMemset(c->vpool, 0, pool_bytes)) != hipSuccess) return fail(e, "hipMemset V pool");
   if (g.C) {
@@ -361,10 +384,28 @@ int gca_attend(gca_cache* c, int64_t frame_idx, const void* q, void* out, float*
   int rc = c->plan.check_attend(frame_idx);
   if (rc) return rc;
   hipStream_t s = (hipStream_t)stream;
-  gca::SelectStep st;
-  rc = do_select(c, s, &st);
-  if (rc) return rc;
   const gca::Geometry& g = c->g;
+  gca::SelectStep st = c->plan.select();
+  const void* qa = q;
+  if (g.rope) {
+    // gather list and rotated queries from one launch
+    gca::RopeArgs ra;
+    ra.x = q;
+    ra.y = c->qrot;
+    ra.frame = frame_idx;
+    ra.T = g.T;
+    ra.H = g.H;
+    ra.tabs = c->tabs;
+    Prof p(c, 2, s);
+    GCA_HIP(gca::launch_prepare(g.dtype, select_args(c, st), ra, s), "prepare kernel launch");
+    qa = c->qrot;
+  } else {
+    Prof p(c, 2, s);
+    GCA_HIP(gca::launch_select(select_args(c, st), s), "select kernel launch");
+  }
+  c->sel_valid = true;
+  c->sel_n = st.n_sel;
+  c->sel_ctx = st.n_ctx;
   int ept = gca::kKeysPerTile / g.P;
   int n_tiles = (st.n_sel + ept - 1) / ept;
   int qpw = gca::queries_per_wg(g.dtype);
@@ -378,7 +419,7 @@ int gca_attend(gca_cache* c, int64_t frame_idx, const void* q, void* out, float*
   int tps = (n_tiles + S - 1) / S;
   S = (n_tiles + tps - 1) / tps;
   gca::AttnArgs a;
-  a.q = q;
+  a.q = qa;
   a.kpool = c->kpool;
   a.vpool = c->vpool;
   a.sel_page = c->sel_page;
@@ -400,8 +441,6 @@ int gca_attend(gca_cache* c, int64_t frame_idx, const void* q, void* out, float*
   a.n_qtiles = qtiles;
   a.n_units = g.H * S;
   a.out_bf16 = g.out_dtype == GCA_BF16;
-  a.rope = g.rope;
-  a.tabs = c->tabs;
   {
     Prof p(c, 3, s);
     GCA_HIP(gca::launch_attn(g.dtype, a, s), "attention kernel launch");
