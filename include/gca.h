@@ -203,13 +203,15 @@ int gca_export_state(gca_cache* cache, gca_state_view* view, gca_stream_t stream
  * [H][P][D] in the cache dtype (slot order), whatever the device layout. */
 int gca_read_page(gca_cache* cache, int32_t page, void* host_k, void* host_v, gca_stream_t stream);
 
-/* Kernel timing with HIP events recorded around every launch on its stream.
+/* Kernel timing with HIP events recorded around launches on their stream.
  * kind: 0 append, 1 evict, 2 selection (inside gca_attend it also rotates
  * the queries), 3 attention, 4 split merge, 5 rope.
- * gca_profile_enable(cache, capacity) starts recording up to `capacity`
- * launches (0 stops); gca_profile_read synchronises and returns the summed
- * milliseconds and launch count of one kind, then forgets them. */
-int gca_profile_enable(gca_cache* cache, int32_t capacity);
+ * gca_profile_enable(cache, capacity, kinds) starts recording up to
+ * `capacity` launches of the kinds whose bit (1 << kind) is set in `kinds`
+ * (capacity 0 stops); gca_profile_read synchronises and returns the summed
+ * milliseconds and launch count of one kind, then forgets them.  Each event
+ * adds a little stream work, so record only the kinds to be measured. */
+int gca_profile_enable(gca_cache* cache, int32_t capacity, uint32_t kinds);
 int gca_profile_read(gca_cache* cache, int32_t kind, double* total_ms, int32_t* count);
 
 /* ---- host-only planner -------------------------------------------------------

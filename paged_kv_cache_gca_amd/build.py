@@ -16,6 +16,9 @@ FLAGS = [
     "-ffp-contract=off",
     # keep the compiler from forming packed fp32 VALU ops
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # per-thread arrays stay in registers: the kernels budget LDS themselves
+    # (two attention workgroups per CU), so no private array is moved there
+    "-mllvm", "-disable-promote-alloca-to-lds",
     "-Wno-unused-command-line-argument",
 ]
 

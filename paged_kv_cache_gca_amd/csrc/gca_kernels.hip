@@ -167,6 +167,21 @@ __global__ __launch_bounds__(256) void k_evict(EvictArgs a) {
     vp[(((size_t)dst * a.H + h) * kHeadDim + d) * a.P + ds] =
         vp[(((size_t)src * a.H + h) * kHeadDim + d) * a.P + ss];
   }
+  // slots of the last written trajectory page past the new end stay zero (a
+  // popped page holds stale data); they are disjoint from the slots copied above
+  const int64_t end = a.traj_len + a.C;
+  const int fill = (int)(end % a.P);
+  if (a.C > 0 && fill != 0) {
+    int pi = (int)((end - 1) / a.P);
+    int dst = pi < a.n_traj_pages ? a.traj_pages[pi]
+                                  : a.ring[(a.ring_head + (pi - a.n_traj_pages)) % a.N];
+    const int n = (a.P - fill) * kHeadDim;
+    for (int idx = tid; idx < n; idx += 256) {
+      int j = idx / kHeadDim, d = idx - j * kHeadDim;
+      kp[(((size_t)dst * a.H + h) * a.P + fill + j) * kHeadDim + d] = from_f<T>(0.f);
+      vp[(((size_t)dst * a.H + h) * kHeadDim + d) * a.P + fill + j] = from_f<T>(0.f);
+    }
+  }
   if (h == 0) {
     for (int i = tid; i < a.new_pages; i += 256)
       a.traj_pages[a.n_traj_pages + i] = a.ring[(a.ring_head + i) % a.N];
@@ -178,17 +193,15 @@ __global__ __launch_bounds__(256) void k_evict(EvictArgs a) {
 // ---------------------------------------------------------------------------
 // Gather list in canonical order: anchors, window oldest -> newest, trajectory.
 
-__global__ __launch_bounds__(256) void k_select(SelectArgs a) {
-  int e = blockIdx.x * 256 + threadIdx.x;
-  if (e >= a.n_sel) return;
+__device__ inline void gather_entry(const SelectArgs& a, int e) {
+  int page = a.zero_page, len = 0;
   int nf = (a.n_anchor + a.win_count) * a.ppf;
-  int page, len;
   if (e < nf) {
     int f = e / a.ppf, i = e - f * a.ppf;
     int slot = f < a.n_anchor ? f : a.A + (a.win_first + (f - a.n_anchor)) % a.Wr;
     page = a.rec_pages[slot * a.ppf + i];
     len = (i == a.ppf - 1) ? a.last_len : a.P;
-  } else {
+  } else if (e < a.n_sel) {
     int ti = e - nf;
     page = a.traj_pages[ti];
     int64_t rem = a.traj_len - (int64_t)ti * a.P;
@@ -198,28 +211,18 @@ __global__ __launch_bounds__(256) void k_select(SelectArgs a) {
   a.sel_len[e] = len;
 }
 
+__global__ __launch_bounds__(256) void k_select(SelectArgs a) {
+  int e = blockIdx.x * 256 + threadIdx.x;
+  if (e < a.n_write) gather_entry(a, e);
+}
+
 // One launch per attention call: blocks [0, sel_blocks) build the gather
 // list, the remaining blocks rotate the frame's queries into a workspace.
 template <typename T>
 __global__ __launch_bounds__(256) void k_prepare(SelectArgs sa, RopeArgs ra, int sel_blocks) {
   if ((int)blockIdx.x < sel_blocks) {
     int e = blockIdx.x * 256 + threadIdx.x;
-    if (e >= sa.n_sel) return;
-    int nf = (sa.n_anchor + sa.win_count) * sa.ppf;
-    int page, len;
-    if (e < nf) {
-      int f = e / sa.ppf, i = e - f * sa.ppf;
-      int slot = f < sa.n_anchor ? f : sa.A + (sa.win_first + (f - sa.n_anchor)) % sa.Wr;
-      page = sa.rec_pages[slot * sa.ppf + i];
-      len = (i == sa.ppf - 1) ? sa.last_len : sa.P;
-    } else {
-      int ti = e - nf;
-      page = sa.traj_pages[ti];
-      int64_t rem = sa.traj_len - (int64_t)ti * sa.P;
-      len = rem < sa.P ? (int)rem : sa.P;
-    }
-    sa.sel_page[e] = page;
-    sa.sel_len[e] = len;
+    if (e < sa.n_write) gather_entry(sa, e);
     return;
   }
   constexpr int EPC = 16 / sizeof(T);
@@ -250,9 +253,8 @@ __global__ void k_ring_init(int32_t* ring, const int32_t* init, int N) {
 // and scaling are per lane plus one exchange with lane ^ 32.  P^T is fed
 // straight from the S^T accumulators as the B operand of O^T = V^T P^T; the
 // key order inside each 16-key chunk follows the accumulator layout, and the
-// V^T operand is read in the same order.  Row sums come from one more MFMA
-// with an all-ones A operand over the same rounded P, so sum(P) and P.V use
-// identical weights.
+// V^T operand is read in the same order.  Row sums are dot products of the
+// same rounded P with ones, so sum(P) and P.V use identical weights.
 
 template <typename T>
 struct Mfma;
@@ -264,12 +266,6 @@ struct Mfma<bf16> {
   __device__ static inline floatx16 mma(Frag a, Frag b, floatx16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
   }
-  __device__ static inline Frag ones() {
-    Frag f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) f[i] = (bf16)1.0f;
-    return f;
-  }
 };
 template <>
 struct Mfma<float> {
@@ -279,7 +275,6 @@ struct Mfma<float> {
   __device__ static inline floatx16 mma(Frag a, Frag b, floatx16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
   }
-  __device__ static inline Frag ones() { return 1.0f; }
 };
 
 // K operand: key row `row`, dims [dc*2*KPL + hi*KPL, +KPL).
@@ -340,6 +335,7 @@ __device__ inline void load_q(const AttnArgs& a, int qbase, int h, int l32, int 
     qf[0][dc] = q < a.Tq ? Q[((size_t)q * a.H + h) * kHeadDim + dc * 2 + hi] : 0.f;
 }
 
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 template <typename T, int P>
 struct TileLoader {
   static constexpr int EPC = 16 / sizeof(T);           // elements per 16-byte chunk
@@ -358,53 +354,42 @@ struct TileLoader {
   __device__ static int v_row(int tid, int i) { return (tid + 256 * i) / CPRV; }
   __device__ static int v_key0(int tid) { return (tid % CPRV) * EPC; }
 
-  int pg_k[NC], pg_v, len_v;  // page ids / valid length of the next tile
-  uint4 kr[NC], vr[NC];
-  int len_me;                 // thread < EPT: valid length of its entry
-  int dlen_v, dlen_me;        // lengths of the tile held in kr / vr
+  const char* kaddr[NC];     // this thread's K chunks inside page 0 (bytes)
+  const char* vaddr;         // its first V^T chunk inside page 0; chunk i is VSTEP bytes on
+  static constexpr int VSTEP = (256 / CPRV) * P * (int)sizeof(T);
+  uint32_t page_bytes;
+  int pg_k[NC], pg_v;         // page ids of the next tile
+  u32x4 kr[NC], vr[NC];       // 16-byte chunks of the next tile (native vectors: plain loads)
+  int len_me;                 // valid length of entry tid % EPT of the next tile
+  int dlen_me;                // the same for the tile held in kr / vr
 
-  // page ids (and lengths) of tile `tile`; entries past the list read page 0
+  __device__ void init(const T* kpool, const T* vpool, int h, int H, int tid) {
+    page_bytes = (uint32_t)(H * P * kHeadDim * sizeof(T));
+#pragma unroll
+    for (int i = 0; i < NC; ++i)
+      kaddr[i] = (const char*)(kpool + ((h * P) + (k_row(tid, i) % P)) * kHeadDim + k_part(tid) * EPC);
+    vaddr = (const char*)(vpool + (h * kHeadDim + v_row(tid, 0)) * P + (v_key0(tid) % P));
+  }
+  // page ids (and lengths) of tile `tile`; the gather list is padded past its end
   __device__ void fetch_pages(const AttnArgs& a, int tile, int tid) {
 #pragma unroll
-    for (int i = 0; i < NC; ++i) {
-      int e = tile * EPT + k_row(tid, i) / P;
-      pg_k[i] = e < a.n_sel ? a.sel_page[e] : 0;
-    }
-    int e = tile * EPT + v_key0(tid) / P;
-    pg_v = e < a.n_sel ? a.sel_page[e] : 0;
-    len_v = e < a.n_sel ? a.sel_len[e] : 0;
-    len_me = 0;
-    if (tid < EPT) {
-      int e2 = tile * EPT + tid;
-      len_me = e2 < a.n_sel ? a.sel_len[e2] : 0;
-    }
+    for (int i = 0; i < NC; ++i) pg_k[i] = a.sel_page[tile * EPT + k_row(tid, i) / P];
+    pg_v = a.sel_page[tile * EPT + v_key0(tid) / P];
+    len_me = a.sel_len[tile * EPT + tid % EPT];
   }
-  __device__ void fetch_data(const T* kpool, const T* vpool, int h, int H, int tid) {
-    const size_t page_elems = (size_t)H * P * kHeadDim;
-    dlen_v = len_v;
+  __device__ void fetch_data(int tid) {
     dlen_me = len_me;
 #pragma unroll
     for (int i = 0; i < NC; ++i) {
-      int r = k_row(tid, i);
-      kr[i] = *(const uint4*)(kpool + (size_t)pg_k[i] * page_elems +
-                              ((h * P) + (r % P)) * kHeadDim + k_part(tid) * EPC);
-      vr[i] = *(const uint4*)(vpool + (size_t)pg_v * page_elems +
-                              (h * kHeadDim + v_row(tid, i)) * P + (v_key0(tid) % P));
+      kr[i] = *(const u32x4*)(kaddr[i] + (uint64_t)(uint32_t)pg_k[i] * page_bytes);
+      vr[i] = *(const u32x4*)(vaddr + (uint64_t)(uint32_t)pg_v * page_bytes + i * VSTEP);
     }
   }
   __device__ void store(T* tileb, int* llen, int tid) {
-    const int slot0 = v_key0(tid) % P;
 #pragma unroll
     for (int i = 0; i < NC; ++i) {
-      *(uint4*)(tileb + k_row(tid, i) * KP + k_part(tid) * EPC) = kr[i];
-      Vec16<T> v;
-      v.u = vr[i];
-      if (slot0 + EPC > dlen_v) {  // keys past the entry's length contribute nothing
-#pragma unroll
-        for (int j = 0; j < EPC; ++j)
-          if (slot0 + j >= dlen_v) v.e[j] = from_f<T>(0.f);
-      }
-      *(uint4*)(tileb + kKeysPerTile * KP + v_row(tid, i) * VP + v_key0(tid)) = v.u;
+      *(u32x4*)(tileb + k_row(tid, i) * KP + k_part(tid) * EPC) = kr[i];
+      *(u32x4*)(tileb + kKeysPerTile * KP + v_row(tid, i) * VP + v_key0(tid)) = vr[i];
     }
     if (tid < EPT) llen[tid] = dlen_me;
   }
@@ -471,9 +456,10 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
   const T* vpool = (const T*)a.vpool;
 
   L ld;
+  ld.init(kpool, vpool, h, a.H, tid);
   if (t0 < t1) {
     ld.fetch_pages(a, t0, tid);
-    ld.fetch_data(kpool, vpool, h, a.H, tid);
+    ld.fetch_data(tid);
     ld.fetch_pages(a, t0 + 1, tid);
   }
   Frag qf[QLDS ? 1 : NQB][QLDS ? 1 : NDC];
@@ -513,7 +499,7 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
     const int buf = tile & 1;
     const bool more = tile + 1 < t1;
     if (more) {
-      ld.fetch_data(kpool, vpool, h, a.H, tid);   // tile + 1, lands during this tile's math
+      ld.fetch_data(tid);                         // tile + 1, lands during this tile's math
       ld.fetch_pages(a, tile + 2, tid);           // page ids two tiles ahead
     }
     const T* ck = lt[buf];
@@ -552,13 +538,16 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
     if (EPT > 1) full = full && lens.y == P;
     if (EPT > 2) full = full && lens.z == P && lens.w == P;
     if (!full) {
-      int lv[4] = {lens.x, lens.y, lens.z, lens.w};
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          int key = kb * 32 + (r >> 2) * 8 + hi * 4 + (r & 3);
-          if ((key % P) >= lv[key / P]) {
+          // key kb*32 + 8*(r/4) + 4*hi + r%4: P is a multiple of 8, so its
+          // entry is known at compile time and only the slot depends on hi
+          const int k8 = kb * 32 + (r >> 2) * 8;
+          const int e = k8 / P;
+          const int len = e == 0 ? lens.x : e == 1 ? lens.y : e == 2 ? lens.z : lens.w;
+          if ((k8 % P) + hi * 4 + (r & 3) >= len) {
 #pragma unroll
             for (int qb = 0; qb < NQB; ++qb) s[kb][qb][r] = -INFINITY;
           }
@@ -727,13 +716,13 @@ hipError_t launch_evict(int dtype, const EvictArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_select(const SelectArgs& a, hipStream_t s) {
-  if (a.n_sel <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_select, dim3((a.n_sel + 255) / 256), dim3(256), 0, s, a);
+  if (a.n_write <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_select, dim3((a.n_write + 255) / 256), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_prepare(int dtype, const SelectArgs& sa, const RopeArgs& ra, hipStream_t s) {
-  int sel_blocks = (sa.n_sel + 255) / 256;
+  int sel_blocks = (sa.n_write + 255) / 256;
   size_t chunks = (size_t)ra.T * ra.H * (dtype ? 8 : 16);
   int rope_blocks = (int)((chunks + 255) / 256);
   dim3 grid(sel_blocks + rope_blocks);

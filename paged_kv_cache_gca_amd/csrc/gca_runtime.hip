@@ -71,6 +71,7 @@ struct gca_cache {
   int64_t sel_ctx = 0;
   // profiling
   int prof_cap = 0;
+  uint32_t prof_kinds = 0;
   std::vector<ProfRec> prof;
   std::vector<hipEvent_t> prof_pool;
 
@@ -122,7 +123,9 @@ void build_rope(const gca::Geometry& g, std::vector<float2>* t, std::vector<floa
 
 void prof_begin(gca_cache* c, int kind, hipStream_t s, ProfRec* r) {
   r->kind = -1;
-  if (c->prof_cap <= 0 || (int)c->prof.size() >= c->prof_cap || c->prof_pool.size() < 2) return;
+  if (c->prof_cap <= 0 || !(c->prof_kinds & (1u << kind)) || (int)c->prof.size() >= c->prof_cap ||
+      c->prof_pool.size() < 2)
+    return;
   r->kind = kind;
   r->b = c->prof_pool.back();
   c->prof_pool.pop_back();
@@ -162,27 +165,14 @@ gca::SelectArgs select_args(gca_cache* c, const gca::SelectStep& st) {
   a.win_count = st.win_count;
   a.n_traj_pages = st.n_traj_pages;
   a.n_sel = st.n_sel;
+  a.n_write = gca::padded_sel(st.n_sel, c->g.P);
+  a.zero_page = c->g.N;
   return a;
 }
 
 int do_select(gca_cache* c, hipStream_t s, gca::SelectStep* out) {
   gca::SelectStep st = c->plan.select();
-  gca::SelectArgs a;
-  a.rec_pages = c->rec_pages;
-  a.traj_pages = c->traj_pages;
-  a.sel_page = c->sel_page;
-  a.sel_len = c->sel_len;
-  a.traj_len = st.traj_len;
-  a.ppf = c->g.ppf;
-  a.P = c->g.P;
-  a.last_len = c->g.last_len;
-  a.A = c->g.A;
-  a.Wr = c->g.Wr;
-  a.n_anchor = st.n_anchor;
-  a.win_first = st.win_first;
-  a.win_count = st.win_count;
-  a.n_traj_pages = st.n_traj_pages;
-  a.n_sel = st.n_sel;
+  gca::SelectArgs a = select_args(c, st);
   {
     Prof p(c, 2, s);
     GCA_HIP(gca::launch_select(a, s), "select kernel launch");
@@ -221,7 +211,9 @@ int gca_cache_create(const gca_config* cfg, gca_cache** out) {
     c->num_cu = cus;
   c->esize = g.dtype == GCA_BF16 ? 2 : 4;
   size_t page_elems = (size_t)g.H * g.P * g.D;
-  size_t pool_bytes = (size_t)g.N * page_elems * c->esize;
+  // pages [0, N) are handed out by the ring; page N stays zero forever and
+  // pads the gather list
+  size_t pool_bytes = ((size_t)g.N + 1) * page_elems * c->esize;
   size_t rows = (size_t)g.T * g.H;
   if ((e = dmalloc(&c->kpool, pool_bytes)) != hipSuccess) return fail(e, "hipMalloc K pool");
   if ((e = dmalloc(&c->vpool, pool_bytes)) != hipSuccess) return fail(e, "hipMalloc V pool");
@@ -232,9 +224,9 @@ int gca_cache_create(const gca_config* cfg, gca_cache** out) {
     return fail(e, "hipMalloc trajectory");
   if ((e = dmalloc(&c->compact, sizeof(int32_t) * (size_t)g.C)) != hipSuccess)
     return fail(e, "hipMalloc compact list");
-  if ((e = dmalloc(&c->sel_page, sizeof(int32_t) * (size_t)g.sel_cap)) != hipSuccess)
+  if ((e = dmalloc(&c->sel_page, sizeof(int32_t) * ((size_t)g.sel_cap + gca::kSelPad))) != hipSuccess)
     return fail(e, "hipMalloc gather list");
-  if ((e = dmalloc(&c->sel_len, sizeof(int32_t) * (size_t)g.sel_cap)) != hipSuccess)
+  if ((e = dmalloc(&c->sel_len, sizeof(int32_t) * ((size_t)g.sel_cap + gca::kSelPad))) != hipSuccess)
     return fail(e, "hipMalloc gather list");
   if ((e = dmalloc(&c->o_part, sizeof(float) * rows * g.D * kMaxSplits)) != hipSuccess)
     return fail(e, "hipMalloc split workspace");
@@ -557,8 +549,9 @@ int gca_read_page(gca_cache* c, int32_t page, void* host_k, void* host_v, gca_st
   return GCA_OK;
 }
 
-int gca_profile_enable(gca_cache* c, int32_t capacity) {
+int gca_profile_enable(gca_cache* c, int32_t capacity, uint32_t kinds) {
   if (!c || capacity < 0) return GCA_ERR_INVALID_ARGUMENT;
+  c->prof_kinds = kinds;
   GCA_HIP(hipDeviceSynchronize(), "profile sync");
   for (auto& r : c->prof) {
     c->prof_pool.push_back(r.a);

@@ -84,7 +84,7 @@ def _load():
         "gca_query": [vp, C.POINTER(gca_info)],
         "gca_export_state": [vp, C.POINTER(gca_state_view), vp],
         "gca_read_page": [vp, i32, vp, vp, vp],
-        "gca_profile_enable": [vp, i32],
+        "gca_profile_enable": [vp, i32, u32],
         "gca_profile_read": [vp, i32, C.POINTER(C.c_double), C.POINTER(i32)],
         "gca_plan_create": [C.POINTER(gca_config), C.POINTER(vp)],
         "gca_plan_destroy": [vp],
@@ -322,8 +322,11 @@ class Cache:
             return kf.reshape(shape), vf.reshape(shape)
         return kb.reshape(shape), vb.reshape(shape)
 
-    def profile_enable(self, capacity: int):
-        _check(_lib.gca_profile_enable(self.h, capacity), "gca_profile_enable")
+    def profile_enable(self, capacity: int, kinds=("append", "evict", "select", "attn", "merge", "rope")):
+        mask = 0
+        for k in kinds:
+            mask |= 1 << KIND[k]
+        _check(_lib.gca_profile_enable(self.h, capacity, mask), "gca_profile_enable")
 
     def profile_read(self, kind: str):
         ms = C.c_double()

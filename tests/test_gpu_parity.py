@@ -79,6 +79,32 @@ def test_small_bf16_stream_parity(P, interval, out_dtype):
     assert kmis <= 1e-3 * ktot, (kmis, ktot)
 
 
+def test_pool_tails_stay_zero_through_recycling():
+    """Every slot past a gather entry's valid length holds zeros, also in pages
+    recycled from earlier frames (the attention kernel relies on it: masked
+    keys meet a zero V row).  24 frames with TEMP frames cycle the ring several
+    times; the trajectory's last page is partial after most evictions."""
+    w = WL.Workload("small_tails", P=16, keyframe_interval=2, **dict(SMALL, n_frames=24, W=2))
+    p = Pair(w)
+    was_frame_page = set()
+    recycled_traj = set()  # trajectory pages that earlier held a frame's tokens
+    partial_checked = 0
+    for f in range(w.n_frames):
+        key = p.step(f)
+        gs = p.check_state()
+        was_frame_page.update(gs["frame_pages"].ravel().tolist())
+        recycled_traj.update(t for t in gs["traj_pages"].tolist() if t in was_frame_page)
+        for page, ln in zip(gs["sel_page"].tolist(), gs["sel_len"].tolist()):
+            if ln < w.P:
+                kp, vp = p.gpu.read_page(page)
+                assert not np.any(kp[:, ln:, :]), (f, page, ln)
+                assert not np.any(vp[:, ln:, :]), (f, page, ln)
+                partial_checked += 1
+        if not key:
+            p.rollback(f)
+    assert partial_checked > 20 and len(recycled_traj) > 0, (partial_checked, len(recycled_traj))
+
+
 def test_ring_window_no_anchor_no_trajectory():
     w = WL.Workload("small_ring", T=300, H=2, D=64, P=64, dtype="bf16", n_frames=10, A=0, W=3, C=0,
                     rope=1, num_special=3, grid_h=9, grid_w=33, seed=22)
