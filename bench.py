@@ -5,8 +5,10 @@ One step = one pass of the whole GCA path over a synthetic frame stream of the
 append (3D RoPE on K, paged scatter) -> evict/compact -> attend (pool
 selection, paged MFMA attention with RoPE on Q, split merge); non-keyframes do
 append -> attend -> rollback.  Inputs are resident in HBM before the timed
-region.  The attention kernel's duration comes from HIP events that the library
-records around each of its launches on the stream it launches on; the roofline
+region.  Each frame is one gca_step call: one launch for the append, eviction,
+query rotation and gather list, then the attention and the split merge.  The
+attention kernel's duration comes from HIP events that the library records
+around each of its launches on the stream it launches on; the roofline
 uses the algorithmic FLOPs 4*T*H*D*n_ctx per frame.  The other kernels'
 durations come from a rocprofv3 kernel trace of the same command.
 
@@ -104,14 +106,8 @@ def run_gpu(w, steps, warmup):
             raise RuntimeError("reset failed")
         for f in range(w.n_frames):
             i = f % n_stage
-            key = w.is_keyframe(f)
-            rc = cache.append_frame(f, K[i], V[i], temp=not key, stream=stream)
-            if rc == 0 and key:
-                rc = cache.evict_compact(stream)
-            if rc == 0:
-                rc = cache.attend(f, Q[i], out, lse, stream)
-            if rc == 0 and not key:
-                rc = cache.rollback_last_frame(f, stream)
+            # append (+ evict) + attend (+ rollback): one update launch, then attention
+            rc = cache.step(f, K[i], V[i], Q[i], out, lse, keyframe=w.is_keyframe(f), stream=stream)
             if rc != 0:
                 raise RuntimeError(f"frame {f}: {gca.status_string(rc)}")
 

@@ -181,6 +181,19 @@ int gca_attend(gca_cache* cache, int64_t frame_idx, const void* q, void* out, fl
  * Errors: SEQUENCE (no TEMP pending or another frame index). */
 int gca_rollback_last_frame(gca_cache* cache, int64_t frame_idx, gca_stream_t stream);
 
+/* One frame of the loop above in a single call: append_frame (as a keyframe
+ * with GCA_STEP_KEYFRAME, then evict_frames; otherwise as GCA_APPEND_TEMP),
+ * compute_attention at frame_idx, and for a non-keyframe
+ * rollback_last_frame.  Results are bit for bit those of the individual calls
+ * in that order.  The whole step is validated on the host before anything is
+ * enqueued, so an error leaves the cache unchanged.  The append, the
+ * eviction, the query rotation and the gather list are enqueued as one
+ * launch, followed by the attention.  k, v, q, out, lse as for
+ * gca_append_frame and gca_attend.  Errors: the union of theirs. */
+enum { GCA_STEP_KEYFRAME = 1u };
+int gca_step(gca_cache* cache, int64_t frame_idx, const void* k, const void* v, const void* q,
+             void* out, float* lse, uint32_t flags, gca_stream_t stream);
+
 /* ---- pieces of the path, for tests and tools ------------------------------- */
 
 /* Build the gather list of the current context on the device (gca_attend does
@@ -205,7 +218,8 @@ int gca_read_page(gca_cache* cache, int32_t page, void* host_k, void* host_v, gc
 
 /* Kernel timing with HIP events recorded around launches on their stream.
  * kind: 0 append, 1 evict, 2 selection (inside gca_attend it also rotates
- * the queries), 3 attention, 4 split merge, 5 rope.
+ * the queries), 3 attention, 4 split merge, 5 rope, 6 the update launch of
+ * gca_step (append, eviction, query rotation and gather list).
  * gca_profile_enable(cache, capacity, kinds) starts recording up to
  * `capacity` launches of the kinds whose bit (1 << kind) is set in `kinds`
  * (capacity 0 stops); gca_profile_read synchronises and returns the summed

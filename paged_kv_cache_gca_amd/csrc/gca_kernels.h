@@ -71,6 +71,13 @@ struct SelectArgs {
   int ppf, P, last_len, A, Wr, n_anchor, win_first, win_count, n_traj_pages, n_sel;
   int n_write;    // padded_sel(n_sel, P): entries written, the tail as (zero_page, 0)
   int zero_page;  // N
+  // Built in the same launch as an append / eviction: page ids not yet in the
+  // page tables are read from the ring where that launch pops them.
+  const int32_t* ring;
+  int N;
+  int64_t newest_pos;  // >= 0: ring position of the newest frame's first page
+  int traj_known;      // trajectory pages whose ids are in traj_pages; the
+  int64_t traj_pos;    // rest start at this ring position
 };
 
 struct AttnArgs {
@@ -114,6 +121,10 @@ hipError_t launch_evict(int dtype, const EvictArgs& a, hipStream_t s);
 hipError_t launch_select(const SelectArgs& a, hipStream_t s);
 // gather list and query rotation (into ra.y) in one launch
 hipError_t launch_prepare(int dtype, const SelectArgs& sa, const RopeArgs& ra, hipStream_t s);
+// One launch: append (if ap), eviction (if ev), query rotation (if ra) and the
+// gather list (if sa) of the state after them; their accesses are disjoint.
+hipError_t launch_update(int dtype, const AppendArgs* ap, const EvictArgs* ev, const RopeArgs* ra,
+                         const SelectArgs* sa, hipStream_t s);
 hipError_t launch_attn(int dtype, const AttnArgs& a, hipStream_t s);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t s);
 hipError_t launch_rope(int dtype, const RopeArgs& a, hipStream_t s);

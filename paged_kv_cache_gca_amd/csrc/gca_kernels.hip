@@ -79,11 +79,11 @@ __device__ inline void rotate_chunk(Vec16<T>& v, const RopeTabs& R, int64_t fram
   }
 }
 
+// 16-byte chunk c of x -> y (rotated); chunks past the tensor are ignored
 template <typename T>
-__global__ __launch_bounds__(256) void k_rope(RopeArgs a) {
+__device__ inline void rope_chunk(const RopeArgs& a, size_t c) {
   constexpr int EPC = 16 / sizeof(T);
   constexpr int CPR = kHeadDim / EPC;
-  size_t c = (size_t)blockIdx.x * 256 + threadIdx.x;
   size_t total = (size_t)a.T * a.H * CPR;
   if (c >= total) return;
   int part = (int)(c % CPR);
@@ -93,6 +93,15 @@ __global__ __launch_bounds__(256) void k_rope(RopeArgs a) {
   rotate_chunk<T>(v, a.tabs, a.frame, tok, part * EPC / 2);
   ((uint4*)a.y)[c] = v.u;
 }
+template <typename T>
+inline size_t rope_chunks(const RopeArgs& a) {
+  return (size_t)a.T * a.H * (kHeadDim / (16 / sizeof(T)));
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void k_rope(RopeArgs a) {
+  rope_chunk<T>(a, (size_t)blockIdx.x * 256 + threadIdx.x);
+}
 
 // ---------------------------------------------------------------------------
 // Append: workgroup (i, h) fills page i of the frame for head h.  K rows are
@@ -101,12 +110,12 @@ __global__ __launch_bounds__(256) void k_rope(RopeArgs a) {
 // frame's last token are zeroed.
 
 template <typename T>
-__global__ __launch_bounds__(256) void k_append(AppendArgs a) {
+__device__ inline void append_block(const AppendArgs& a, int i, int h) {
   constexpr int EPC = 16 / sizeof(T);
   constexpr int CPR = kHeadDim / EPC;
   constexpr int LP = kHeadDim + EPC;  // LDS row pitch
   __shared__ __attribute__((aligned(16))) T lds[64 * LP];
-  const int i = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+  const int tid = threadIdx.x;
   const int page = a.ring[(a.ring_pos + i) % a.N];
   if (h == 0 && tid == 0) a.rec_pages[a.slot * a.ppf + i] = page;
   const T* K = (const T*)a.k;
@@ -140,6 +149,11 @@ __global__ __launch_bounds__(256) void k_append(AppendArgs a) {
   }
 }
 
+template <typename T>
+__global__ __launch_bounds__(256) void k_append(AppendArgs a) {
+  append_block<T>(a, blockIdx.x, blockIdx.y);
+}
+
 // ---------------------------------------------------------------------------
 // Evict one frame: workgroup h copies the C compact tokens of head h; block 0
 // also records the trajectory pages it pops and pushes the frame's pages to
@@ -148,8 +162,8 @@ __global__ __launch_bounds__(256) void k_append(AppendArgs a) {
 // the evicted frame's own pages are live while it is evicted.
 
 template <typename T>
-__global__ __launch_bounds__(256) void k_evict(EvictArgs a) {
-  const int h = blockIdx.x, tid = threadIdx.x;
+__device__ inline void evict_block(const EvictArgs& a, int h) {
+  const int tid = threadIdx.x;
   T* kp = (T*)a.kpool;
   T* vp = (T*)a.vpool;
   for (int idx = tid; idx < a.C * kHeadDim; idx += 256) {
@@ -190,20 +204,27 @@ __global__ __launch_bounds__(256) void k_evict(EvictArgs a) {
   }
 }
 
+template <typename T>
+__global__ __launch_bounds__(256) void k_evict(EvictArgs a) {
+  evict_block<T>(a, blockIdx.x);
+}
+
 // ---------------------------------------------------------------------------
 // Gather list in canonical order: anchors, window oldest -> newest, trajectory.
 
 __device__ inline void gather_entry(const SelectArgs& a, int e) {
   int page = a.zero_page, len = 0;
-  int nf = (a.n_anchor + a.win_count) * a.ppf;
+  const int nfr = a.n_anchor + a.win_count;
+  int nf = nfr * a.ppf;
   if (e < nf) {
     int f = e / a.ppf, i = e - f * a.ppf;
     int slot = f < a.n_anchor ? f : a.A + (a.win_first + (f - a.n_anchor)) % a.Wr;
-    page = a.rec_pages[slot * a.ppf + i];
+    page = (a.newest_pos >= 0 && f == nfr - 1) ? a.ring[(a.newest_pos + i) % a.N]
+                                               : a.rec_pages[slot * a.ppf + i];
     len = (i == a.ppf - 1) ? a.last_len : a.P;
   } else if (e < a.n_sel) {
     int ti = e - nf;
-    page = a.traj_pages[ti];
+    page = ti < a.traj_known ? a.traj_pages[ti] : a.ring[(a.traj_pos + (ti - a.traj_known)) % a.N];
     int64_t rem = a.traj_len - (int64_t)ti * a.P;
     len = rem < a.P ? (int)rem : a.P;
   }
@@ -225,17 +246,37 @@ __global__ __launch_bounds__(256) void k_prepare(SelectArgs sa, RopeArgs ra, int
     if (e < sa.n_write) gather_entry(sa, e);
     return;
   }
-  constexpr int EPC = 16 / sizeof(T);
-  constexpr int CPR = kHeadDim / EPC;
-  size_t c = (size_t)(blockIdx.x - sel_blocks) * 256 + threadIdx.x;
-  size_t total = (size_t)ra.T * ra.H * CPR;
-  if (c >= total) return;
-  int part = (int)(c % CPR);
-  int tok = (int)(c / CPR / ra.H);
-  Vec16<T> v;
-  v.u = ((const uint4*)ra.x)[c];
-  rotate_chunk<T>(v, ra.tabs, ra.frame, tok, part * EPC / 2);
-  ((uint4*)ra.y)[c] = v.u;
+  rope_chunk<T>(ra, (size_t)(blockIdx.x - sel_blocks) * 256 + threadIdx.x);
+}
+
+// The per-frame update as one launch.  Block ranges: [0, na) append blocks
+// (page i = b % ppf, head b / ppf), [na, na + ne) eviction blocks (head),
+// [.., + nr) query rotation chunks, [.., + ns) gather-list entries.  The
+// append writes the new frame's pages and record slot; the eviction reads
+// the oldest window frame's pages, writes trajectory pages popped after the
+// append's and pushes to the ring tail; the gather list reads page ids that
+// are not in the page tables yet from the ring positions those pops use.
+template <typename T>
+__global__ __launch_bounds__(256) void k_update(AppendArgs ap, EvictArgs ev, RopeArgs ra, SelectArgs sa,
+                                                 int na, int ne, int nr) {
+  int b = blockIdx.x;
+  if (b < na) {
+    append_block<T>(ap, b % ap.ppf, b / ap.ppf);
+    return;
+  }
+  b -= na;
+  if (b < ne) {
+    evict_block<T>(ev, b);
+    return;
+  }
+  b -= ne;
+  if (b < nr) {
+    rope_chunk<T>(ra, (size_t)b * 256 + threadIdx.x);
+    return;
+  }
+  b -= nr;
+  const int e = b * 256 + threadIdx.x;
+  if (e < sa.n_write) gather_entry(sa, e);
 }
 
 __global__ void k_ring_init(int32_t* ring, const int32_t* init, int N) {
@@ -718,6 +759,27 @@ hipError_t launch_evict(int dtype, const EvictArgs& a, hipStream_t s) {
 hipError_t launch_select(const SelectArgs& a, hipStream_t s) {
   if (a.n_write <= 0) return hipSuccess;
   hipLaunchKernelGGL(k_select, dim3((a.n_write + 255) / 256), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_update(int dtype, const AppendArgs* ap, const EvictArgs* ev, const RopeArgs* ra,
+                         const SelectArgs* sa, hipStream_t s) {
+  AppendArgs a0{};
+  EvictArgs e0{};
+  RopeArgs r0{};
+  SelectArgs s0{};
+  const int na = ap ? ap->ppf * ap->H : 0;
+  const int ne = ev ? ev->H : 0;
+  const int nr = ra ? (int)(((dtype ? rope_chunks<bf16>(*ra) : rope_chunks<float>(*ra)) + 255) / 256) : 0;
+  const int ns = sa ? (sa->n_write + 255) / 256 : 0;
+  const int nb = na + ne + nr + ns;
+  if (nb == 0) return hipSuccess;
+  if (dtype)
+    hipLaunchKernelGGL(k_update<bf16>, dim3(nb), dim3(256), 0, s, ap ? *ap : a0, ev ? *ev : e0, ra ? *ra : r0,
+                       sa ? *sa : s0, na, ne, nr);
+  else
+    hipLaunchKernelGGL(k_update<float>, dim3(nb), dim3(256), 0, s, ap ? *ap : a0, ev ? *ev : e0, ra ? *ra : r0,
+                       sa ? *sa : s0, na, ne, nr);
   return hipGetLastError();
 }
 

@@ -167,7 +167,125 @@ gca::SelectArgs select_args(gca_cache* c, const gca::SelectStep& st) {
   a.n_sel = st.n_sel;
   a.n_write = gca::padded_sel(st.n_sel, c->g.P);
   a.zero_page = c->g.N;
+  a.ring = c->ring;
+  a.N = c->g.N;
+  a.newest_pos = -1;  // all page ids are in the page tables
+  a.traj_known = st.n_traj_pages;
+  a.traj_pos = 0;
   return a;
+}
+
+gca::AppendArgs append_args(gca_cache* c, const gca::AppendStep& st, const void* k, const void* v) {
+  gca::AppendArgs a;
+  a.k = k;
+  a.v = v;
+  a.kpool = c->kpool;
+  a.vpool = c->vpool;
+  a.ring = c->ring;
+  a.rec_pages = c->rec_pages;
+  a.ring_pos = st.ring_pos % c->g.N;
+  a.frame = st.frame;
+  a.N = c->g.N;
+  a.slot = st.slot;
+  a.ppf = c->g.ppf;
+  a.T = c->g.T;
+  a.H = c->g.H;
+  a.P = c->g.P;
+  a.rope = c->g.rope;
+  a.tabs = c->tabs;
+  return a;
+}
+
+gca::EvictArgs evict_args(gca_cache* c, const gca::EvictStep& st) {
+  gca::EvictArgs a;
+  a.kpool = c->kpool;
+  a.vpool = c->vpool;
+  a.ring = c->ring;
+  a.rec_pages = c->rec_pages;
+  a.traj_pages = c->traj_pages;
+  a.compact = c->compact;
+  a.traj_len = st.traj_len;
+  a.ring_head = st.ring_head % c->g.N;
+  a.ring_tail = st.ring_tail % c->g.N;
+  a.N = c->g.N;
+  a.slot = st.slot;
+  a.ppf = c->g.ppf;
+  a.n_traj_pages = st.n_traj_pages;
+  a.new_pages = st.new_pages;
+  a.C = c->g.C;
+  a.H = c->g.H;
+  a.P = c->g.P;
+  return a;
+}
+
+gca::RopeArgs rope_args(gca_cache* c, int64_t frame_idx, const void* x, void* y) {
+  gca::RopeArgs ra;
+  ra.x = x;
+  ra.y = y;
+  ra.frame = frame_idx;
+  ra.T = c->g.T;
+  ra.H = c->g.H;
+  ra.tabs = c->tabs;
+  return ra;
+}
+
+// Attention over the gather list already built for `st` (queries qa already
+// rotated when rope = 1), then the split merge.
+int attend_launch(gca_cache* c, int64_t frame_idx, const void* qa, void* out, float* lse,
+                  const gca::SelectStep& st, hipStream_t s) {
+  const gca::Geometry& g = c->g;
+  int ept = gca::kKeysPerTile / g.P;
+  int n_tiles = (st.n_sel + ept - 1) / ept;
+  int qpw = gca::queries_per_wg(g.dtype);
+  int qtiles = (g.T + qpw - 1) / qpw;
+  // split the context so that about two workgroups run per compute unit
+  int base = qtiles * g.H;
+  int S = (2 * c->num_cu + base - 1) / base;
+  S = std::min(S, kMaxSplits);
+  S = std::min(S, std::max(1, n_tiles / 2));
+  S = std::max(S, 1);
+  int tps = (n_tiles + S - 1) / S;
+  S = (n_tiles + tps - 1) / tps;
+  gca::AttnArgs a;
+  a.q = qa;
+  a.kpool = c->kpool;
+  a.vpool = c->vpool;
+  a.sel_page = c->sel_page;
+  a.sel_len = c->sel_len;
+  a.o_part = c->o_part;
+  a.lse_part = c->lse_part;
+  a.out = out;
+  a.lse = lse;
+  a.frame = frame_idx;
+  a.sm_scale = g.scale;
+  a.c2 = (float)((double)g.scale * 1.4426950408889634);
+  a.Tq = g.T;
+  a.H = g.H;
+  a.P = g.P;
+  a.n_sel = st.n_sel;
+  a.n_tiles = n_tiles;
+  a.tiles_per_split = tps;
+  a.S = S;
+  a.n_qtiles = qtiles;
+  a.n_units = g.H * S;
+  a.out_bf16 = g.out_dtype == GCA_BF16;
+  {
+    Prof p(c, 3, s);
+    GCA_HIP(gca::launch_attn(g.dtype, a, s), "attention kernel launch");
+  }
+  if (S > 1) {
+    gca::MergeArgs m;
+    m.o_part = c->o_part;
+    m.lse_part = c->lse_part;
+    m.out = out;
+    m.lse = lse;
+    m.rows = g.T * g.H;
+    m.S = S;
+    m.out_bf16 = a.out_bf16;
+    Prof p(c, 4, s);
+    GCA_HIP(gca::launch_merge(m, s), "merge kernel launch");
+  }
+  return GCA_OK;
 }
 
 int do_select(gca_cache* c, hipStream_t s, gca::SelectStep* out) {
@@ -304,23 +422,7 @@ int gca_append_frame(gca_cache* c, int64_t frame_idx, const void* k, const void*
   int rc = c->plan.check_append(frame_idx, temp, &st);
   if (rc) return rc;
   hipStream_t s = (hipStream_t)stream;
-  gca::AppendArgs a;
-  a.k = k;
-  a.v = v;
-  a.kpool = c->kpool;
-  a.vpool = c->vpool;
-  a.ring = c->ring;
-  a.rec_pages = c->rec_pages;
-  a.ring_pos = st.ring_pos % c->g.N;
-  a.frame = frame_idx;
-  a.N = c->g.N;
-  a.slot = st.slot;
-  a.ppf = c->g.ppf;
-  a.T = c->g.T;
-  a.H = c->g.H;
-  a.P = c->g.P;
-  a.rope = c->g.rope;
-  a.tabs = c->tabs;
+  gca::AppendArgs a = append_args(c, st, k, v);
   {
     Prof p(c, 0, s);
     GCA_HIP(gca::launch_append(c->g.dtype, a, s), "append kernel launch");
@@ -337,24 +439,7 @@ int gca_evict_compact(gca_cache* c, gca_stream_t stream) {
   if (rc) return rc;
   hipStream_t s = (hipStream_t)stream;
   for (const gca::EvictStep& st : steps) {
-    gca::EvictArgs a;
-    a.kpool = c->kpool;
-    a.vpool = c->vpool;
-    a.ring = c->ring;
-    a.rec_pages = c->rec_pages;
-    a.traj_pages = c->traj_pages;
-    a.compact = c->compact;
-    a.traj_len = st.traj_len;
-    a.ring_head = st.ring_head % c->g.N;
-    a.ring_tail = st.ring_tail % c->g.N;
-    a.N = c->g.N;
-    a.slot = st.slot;
-    a.ppf = c->g.ppf;
-    a.n_traj_pages = st.n_traj_pages;
-    a.new_pages = st.new_pages;
-    a.C = c->g.C;
-    a.H = c->g.H;
-    a.P = c->g.P;
+    gca::EvictArgs a = evict_args(c, st);
     Prof p(c, 1, s);
     GCA_HIP(gca::launch_evict(c->g.dtype, a, s), "evict kernel launch");
   }
@@ -381,13 +466,7 @@ int gca_attend(gca_cache* c, int64_t frame_idx, const void* q, void* out, float*
   const void* qa = q;
   if (g.rope) {
     // gather list and rotated queries from one launch
-    gca::RopeArgs ra;
-    ra.x = q;
-    ra.y = c->qrot;
-    ra.frame = frame_idx;
-    ra.T = g.T;
-    ra.H = g.H;
-    ra.tabs = c->tabs;
+    gca::RopeArgs ra = rope_args(c, frame_idx, q, c->qrot);
     Prof p(c, 2, s);
     GCA_HIP(gca::launch_prepare(g.dtype, select_args(c, st), ra, s), "prepare kernel launch");
     qa = c->qrot;
@@ -398,58 +477,7 @@ int gca_attend(gca_cache* c, int64_t frame_idx, const void* q, void* out, float*
   c->sel_valid = true;
   c->sel_n = st.n_sel;
   c->sel_ctx = st.n_ctx;
-  int ept = gca::kKeysPerTile / g.P;
-  int n_tiles = (st.n_sel + ept - 1) / ept;
-  int qpw = gca::queries_per_wg(g.dtype);
-  int qtiles = (g.T + qpw - 1) / qpw;
-  // split the context so that about two workgroups run per compute unit
-  int base = qtiles * g.H;
-  int S = (2 * c->num_cu + base - 1) / base;
-  S = std::min(S, kMaxSplits);
-  S = std::min(S, std::max(1, n_tiles / 2));
-  S = std::max(S, 1);
-  int tps = (n_tiles + S - 1) / S;
-  S = (n_tiles + tps - 1) / tps;
-  gca::AttnArgs a;
-  a.q = qa;
-  a.kpool = c->kpool;
-  a.vpool = c->vpool;
-  a.sel_page = c->sel_page;
-  a.sel_len = c->sel_len;
-  a.o_part = c->o_part;
-  a.lse_part = c->lse_part;
-  a.out = out;
-  a.lse = lse;
-  a.frame = frame_idx;
-  a.sm_scale = g.scale;
-  a.c2 = (float)((double)g.scale * 1.4426950408889634);
-  a.Tq = g.T;
-  a.H = g.H;
-  a.P = g.P;
-  a.n_sel = st.n_sel;
-  a.n_tiles = n_tiles;
-  a.tiles_per_split = tps;
-  a.S = S;
-  a.n_qtiles = qtiles;
-  a.n_units = g.H * S;
-  a.out_bf16 = g.out_dtype == GCA_BF16;
-  {
-    Prof p(c, 3, s);
-    GCA_HIP(gca::launch_attn(g.dtype, a, s), "attention kernel launch");
-  }
-  if (S > 1) {
-    gca::MergeArgs m;
-    m.o_part = c->o_part;
-    m.lse_part = c->lse_part;
-    m.out = out;
-    m.lse = lse;
-    m.rows = g.T * g.H;
-    m.S = S;
-    m.out_bf16 = a.out_bf16;
-    Prof p(c, 4, s);
-    GCA_HIP(gca::launch_merge(m, s), "merge kernel launch");
-  }
-  return GCA_OK;
+  return attend_launch(c, frame_idx, qa, out, lse, st, s);
 }
 
 int gca_rollback_last_frame(gca_cache* c, int64_t frame_idx, gca_stream_t stream) {
@@ -461,6 +489,64 @@ int gca_rollback_last_frame(gca_cache* c, int64_t frame_idx, gca_stream_t stream
   // returns them, and the frame's record slot is simply no longer live.
   c->plan.commit_rollback();
   c->sel_valid = false;
+  return GCA_OK;
+}
+
+int gca_step(gca_cache* c, int64_t frame_idx, const void* k, const void* v, const void* q, void* out,
+             float* lse, uint32_t flags, gca_stream_t stream) {
+  if (!c || !aligned16(k) || !aligned16(v) || !aligned16(q) || !aligned16(out) ||
+      (lse && ((uintptr_t)lse & 3)) || (flags & ~GCA_STEP_KEYFRAME))
+    return GCA_ERR_INVALID_ARGUMENT;
+  const bool key = flags & GCA_STEP_KEYFRAME;
+  const gca::Geometry& g = c->g;
+  // the whole step on a copy of the planner first: nothing is enqueued or
+  // changed unless every part is valid
+  gca::Planner p = c->plan;
+  gca::AppendStep as;
+  int rc = p.check_append(frame_idx, !key, &as);
+  if (rc) return rc;
+  p.commit_append(as, !key);
+  std::vector<gca::EvictStep> ev;
+  if (key) {
+    if ((rc = p.check_evict(&ev))) return rc;
+    p.commit_evict(ev);
+  }
+  if ((rc = p.check_attend(frame_idx))) return rc;
+  if (!key && (rc = p.check_rollback(frame_idx))) return rc;
+
+  hipStream_t s = (hipStream_t)stream;
+  if (ev.size() > 1) {
+    // several evictions depend on one another: the individual calls
+    if ((rc = gca_append_frame(c, frame_idx, k, v, 0, stream))) return rc;
+    if ((rc = gca_evict_compact(c, stream))) return rc;
+    return gca_attend(c, frame_idx, q, out, lse, stream);
+  }
+  const gca::SelectStep st = p.select();
+  gca::AppendArgs aa = append_args(c, as, k, v);
+  gca::EvictArgs ea{};
+  if (!ev.empty()) ea = evict_args(c, ev[0]);
+  gca::RopeArgs ra = rope_args(c, frame_idx, q, c->qrot);
+  gca::SelectArgs sa = select_args(c, st);
+  sa.newest_pos = as.ring_pos % g.N;
+  if (!ev.empty()) {
+    sa.traj_known = ev[0].n_traj_pages;
+    sa.traj_pos = ev[0].ring_head % g.N;
+  }
+  {
+    Prof pr(c, 6, s);
+    GCA_HIP(gca::launch_update(g.dtype, &aa, ev.empty() ? nullptr : &ea, g.rope ? &ra : nullptr, &sa, s),
+            "update kernel launch");
+  }
+  c->plan = p;
+  c->sel_valid = true;
+  c->sel_n = st.n_sel;
+  c->sel_ctx = st.n_ctx;
+  rc = attend_launch(c, frame_idx, g.rope ? (const void*)c->qrot : q, out, lse, st, s);
+  if (rc) return rc;
+  if (!key) {
+    c->plan.commit_rollback();
+    c->sel_valid = false;
+  }
   return GCA_OK;
 }
 

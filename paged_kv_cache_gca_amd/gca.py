@@ -23,7 +23,8 @@ GCA_ERR_HIP = -5
 GCA_ERR_UNSUPPORTED = -6
 GCA_F32, GCA_BF16 = 0, 1
 GCA_APPEND_TEMP = 1
-KIND = {"append": 0, "evict": 1, "select": 2, "attn": 3, "merge": 4, "rope": 5}
+STEP_KEYFRAME = 1
+KIND = {"append": 0, "evict": 1, "select": 2, "attn": 3, "merge": 4, "rope": 5, "update": 6}
 
 
 class GCAError(RuntimeError):
@@ -79,6 +80,7 @@ def _load():
         "gca_evict_compact": [vp, vp],
         "gca_attend": [vp, i64, vp, vp, vp, vp],
         "gca_rollback_last_frame": [vp, i64, vp],
+        "gca_step": [vp, i64, vp, vp, vp, vp, vp, u32, vp],
         "gca_select": [vp, vp],
         "gca_rope3d": [vp, i64, vp, vp, vp],
         "gca_query": [vp, C.POINTER(gca_info)],
@@ -266,6 +268,11 @@ class Cache:
 
     def rollback_last_frame(self, frame: int, stream=None) -> int:
         return _lib.gca_rollback_last_frame(self.h, frame, _stream(stream))
+
+    def step(self, frame: int, k, v, q, out, lse=None, keyframe: bool = True, stream=None) -> int:
+        """append (+ evict) + attend (+ rollback for a non-keyframe) in one call"""
+        return _lib.gca_step(self.h, frame, _ptr(k), _ptr(v), _ptr(q), _ptr(out), _ptr(lse),
+                             STEP_KEYFRAME if keyframe else 0, _stream(stream))
 
     def select(self, stream=None) -> int:
         return _lib.gca_select(self.h, _stream(stream))

@@ -308,3 +308,78 @@ def test_device_error_paths_change_nothing():
     p.orc.reset()
     p.step(0)
     p.check_state()
+
+
+@pytest.mark.parametrize("rope,interval", [(1, 2), (0, 1)])
+def test_step_matches_individual_calls_bitwise(rope, interval):
+    """gca_step (one launch for append, eviction, query rotation and gather
+    list, then the attention) gives the individual calls' results bit for bit:
+    outputs, lse, page tables, ring, gather list and the pool pages."""
+    w = WL.Workload(f"step_r{rope}_k{interval}", P=16, keyframe_interval=interval,
+                    **dict(SMALL, n_frames=16, W=2, rope=rope))
+    g = gca()
+    cfg = g.Config.from_workload(w)
+    ca, cb = g.Cache(cfg), g.Cache(cfg)
+    fs = stream_of(w)
+    for f in range(w.n_frames):
+        k, v = fs.kv(f)
+        kd, vd, qd = dev(k, "bf16"), dev(v, "bf16"), dev(fs.q(f), "bf16")
+        key = w.is_keyframe(f)
+        oa = torch.empty((w.T, w.H, w.D), dtype=torch.float32, device="cuda")
+        ob = torch.empty_like(oa)
+        la = torch.empty((w.T, w.H), dtype=torch.float32, device="cuda")
+        lb = torch.empty_like(la)
+        assert ca.append_frame(f, kd, vd, temp=not key) == 0
+        if key:
+            assert ca.evict_compact() == 0
+        assert ca.attend(f, qd, oa, la) == 0
+        if not key:
+            assert ca.rollback_last_frame(f) == 0
+        assert cb.step(f, kd, vd, qd, ob, lb, keyframe=key) == 0
+        assert torch.equal(oa, ob) and torch.equal(la, lb), f
+        sa, sb = ca.export_state(), cb.export_state()
+        for name in ("free", "frame_idx", "frame_pages", "traj_pages"):
+            np.testing.assert_array_equal(sa[name], sb[name], err_msg=f"{name} frame {f}")
+        if key:  # the gather list of the step's attention is exported unchanged
+            np.testing.assert_array_equal(sa["sel_page"], sb["sel_page"])
+            np.testing.assert_array_equal(sa["sel_len"], sb["sel_len"])
+    st = ca.export_state()
+    pages = set(st["frame_pages"].ravel().tolist()) | set(st["traj_pages"].tolist())
+    for page in sorted(pages):
+        ka, va = ca.read_page(page)
+        kb, vb = cb.read_page(page)
+        assert np.array_equal(ka, kb) and np.array_equal(va, vb), page
+    assert len(st["traj_pages"]) > 1
+    ca.close()
+    cb.close()
+
+
+def test_step_errors_change_nothing():
+    w = WL.Workload("step_err", P=16, keyframe_interval=1, **dict(SMALL, n_frames=6))
+    g = gca()
+    c = g.Cache(g.Config.from_workload(w))
+    fs = stream_of(w)
+    out = torch.empty((w.T, w.H, w.D), dtype=torch.float32, device="cuda")
+    k, v = fs.kv(0)
+    kd, vd, qd = dev(k, "bf16"), dev(v, "bf16"), dev(fs.q(0), "bf16")
+    assert c.step(0, kd, vd, qd, out) == 0
+    before = c.export_state()
+    info0 = c.query()
+    # frame index not above the last one, unknown flag bit, misaligned pointer
+    assert c.step(0, kd, vd, qd, out) == g.GCA_ERR_SEQUENCE
+    assert _lib_step(c, 1, kd, vd, qd, out, flags=4) == g.GCA_ERR_INVALID_ARGUMENT
+    assert _lib_step(c, 1, kd, vd, qd, out, q_offset=2) == g.GCA_ERR_INVALID_ARGUMENT
+    after = c.export_state()
+    for name in ("free", "frame_idx", "frame_pages", "traj_pages", "sel_page", "sel_len"):
+        np.testing.assert_array_equal(before[name], after[name])
+    assert c.query().last_frame == info0.last_frame
+    assert c.step(1, kd, vd, qd, out) == 0
+    c.close()
+
+
+def _lib_step(c, frame, k, v, q, out, flags=1, q_offset=0):
+    import ctypes
+    g = gca()
+    return g._lib.gca_step(c.h, frame, ctypes.c_void_p(k.data_ptr()), ctypes.c_void_p(v.data_ptr()),
+                           ctypes.c_void_p(q.data_ptr() + q_offset), ctypes.c_void_p(out.data_ptr()),
+                           None, flags, None)
