@@ -479,15 +479,28 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
   constexpr bool QLDS = sizeof(T) == 2;
   __shared__ __attribute__((aligned(16))) Frag lq[QLDS ? kWaves * NQB * NDC * 64 : 1];
 
-  // workgroup -> (head, split, q tile): the q tiles of one (head, split) are
-  // consecutive on one XCD (dispatch is round-robin over XCDs), so they share
-  // that XCD's L2 copy of the split's K/V pages.
+  // workgroup -> (head, split, q tile).  Dispatch is round-robin over the
+  // XCDs, each with its own L2.  With H a multiple of 8, all workgroups of a
+  // head run on one XCD (XCD = h % 8), so both its K/V pages and each q
+  // tile's queries come from HBM once and are shared through that L2; the q
+  // tiles of one split are dispatched consecutively.  Otherwise the q tiles
+  // of one (head, split) share an XCD.
   const int b = blockIdx.x;
   const int xcd = b % kNumXcd, kx = b / kNumXcd;
-  const int unit = (kx / a.n_qtiles) * kNumXcd + xcd;
-  const int qt = kx % a.n_qtiles;
-  if (unit >= a.n_units) return;
-  const int h = unit / a.S, split = unit % a.S;
+  int h, split, qt;
+  if (a.head_major) {
+    const int per = a.S * a.n_qtiles, j = kx % per;
+    h = xcd + kNumXcd * (kx / per);
+    split = j / a.n_qtiles;
+    qt = j % a.n_qtiles;
+    if (h >= a.H) return;
+  } else {
+    const int unit = (kx / a.n_qtiles) * kNumXcd + xcd;
+    if (unit >= a.n_units) return;
+    qt = kx % a.n_qtiles;
+    h = unit / a.S;
+    split = unit % a.S;
+  }
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hi = lane >> 5;
   const int t0 = split * a.tiles_per_split;

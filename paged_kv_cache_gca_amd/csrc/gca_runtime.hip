@@ -269,6 +269,7 @@ int attend_launch(gca_cache* c, int64_t frame_idx, const void* qa, void* out, fl
   a.n_qtiles = qtiles;
   a.n_units = g.H * S;
   a.out_bf16 = g.out_dtype == GCA_BF16;
+  a.head_major = g.H % gca::kNumXcd == 0;
   {
     Prof p(c, 3, s);
     GCA_HIP(gca::launch_attn(g.dtype, a, s), "attention kernel launch");
