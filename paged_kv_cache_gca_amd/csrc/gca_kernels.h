@@ -94,6 +94,7 @@ struct AttnArgs {
   float sm_scale;      // > 0
   float c2;            // sm_scale * log2(e)
   int Tq, H, P, n_sel, n_tiles, tiles_per_split, S, n_qtiles, n_units;
+  int t_odd;           // > 0: even splits hold tiles_per_split tiles, odd ones t_odd
   int out_bf16;
   int head_major;      // H % 8 == 0: all workgroups of a head on one XCD
 };

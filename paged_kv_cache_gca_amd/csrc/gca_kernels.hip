@@ -485,14 +485,31 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
   // tile's queries come from HBM once and are shared through that L2; the q
   // tiles of one split are dispatched consecutively.  Otherwise the q tiles
   // of one (head, split) share an XCD.
+  //
+  // Split sizes (head-major, S even): the even splits of every (head, q tile)
+  // are dispatched first, as the first workgroup of their CU, and hold
+  // t_even tiles; the odd ones come second and hold t_odd.  Two workgroups
+  // share a CU and the first one dispatched issues ahead of the other, so
+  // uneven splits let both finish together.  Boundaries depend only on the
+  // launch parameters: results stay deterministic.
   const int b = blockIdx.x;
   const int xcd = b % kNumXcd, kx = b / kNumXcd;
   int h, split, qt;
   if (a.head_major) {
-    const int per = a.S * a.n_qtiles, j = kx % per;
-    h = xcd + kNumXcd * (kx / per);
-    split = j / a.n_qtiles;
-    qt = j % a.n_qtiles;
+    const int per = a.S * a.n_qtiles;           // workgroups of one head
+    const int nh = (a.H + kNumXcd - 1) / kNumXcd;  // heads on this XCD
+    if (a.t_odd > 0) {
+      const int halfw = nh * per / 2;             // even (then odd) splits of all those heads
+      const int odd = kx / halfw, r = kx % halfw, j = r % (per / 2);
+      h = xcd + kNumXcd * (r / (per / 2));
+      split = 2 * (j / a.n_qtiles) + odd;
+      qt = j % a.n_qtiles;
+    } else {
+      const int j = kx % per;
+      h = xcd + kNumXcd * (kx / per);
+      split = j / a.n_qtiles;
+      qt = j % a.n_qtiles;
+    }
     if (h >= a.H) return;
   } else {
     const int unit = (kx / a.n_qtiles) * kNumXcd + xcd;
@@ -503,8 +520,9 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
   }
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hi = lane >> 5;
-  const int t0 = split * a.tiles_per_split;
-  const int t1 = min(a.n_tiles, t0 + a.tiles_per_split);
+  const int t0 = a.t_odd > 0 ? (split >> 1) * (a.tiles_per_split + a.t_odd) + (split & 1) * a.tiles_per_split
+                             : split * a.tiles_per_split;
+  const int t1 = min(a.n_tiles, t0 + ((split & 1) && a.t_odd > 0 ? a.t_odd : a.tiles_per_split));
   const int qbase = (qt * kWaves + wave) * QPW;
   const T* kpool = (const T*)a.kpool;
   const T* vpool = (const T*)a.vpool;

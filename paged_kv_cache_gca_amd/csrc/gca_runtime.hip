@@ -10,6 +10,7 @@
 #include <cstdio>
 #include <cstring>
 #include <string>
+#include <cstdlib>
 #include <vector>
 
 #include "../../include/gca.h"
@@ -66,6 +67,8 @@ struct gca_cache {
   float* o_part = nullptr;
   float* lse_part = nullptr;
   void* qrot = nullptr;  // rotated queries of the current attention call
+  // tiles of a first-dispatched split per tile of a second-dispatched one
+  float split_ratio = 1.7f;
   bool sel_valid = false;
   int sel_n = 0;
   int64_t sel_ctx = 0;
@@ -270,6 +273,17 @@ int attend_launch(gca_cache* c, int64_t frame_idx, const void* qa, void* out, fl
   a.n_units = g.H * S;
   a.out_bf16 = g.out_dtype == GCA_BF16;
   a.head_major = g.H % gca::kNumXcd == 0;
+  a.t_odd = 0;
+  if (a.head_major && S % 2 == 0 && c->split_ratio > 1.0f) {
+    // pairs of splits: the first dispatched (even) split takes ratio / (1 + ratio)
+    const int pair = (2 * n_tiles + S - 1) / S;
+    int te = (int)((float)pair * c->split_ratio / (1.0f + c->split_ratio) + 0.5f);
+    te = std::min(std::max(te, 1), pair);
+    if (pair - te >= 1) {
+      a.tiles_per_split = te;
+      a.t_odd = pair - te;
+    }
+  }
   {
     Prof p(c, 3, s);
     GCA_HIP(gca::launch_attn(g.dtype, a, s), "attention kernel launch");
@@ -329,6 +343,10 @@ int gca_cache_create(const gca_config* cfg, gca_cache** out) {
       cus > 0)
     c->num_cu = cus;
   c->esize = g.dtype == GCA_BF16 ? 2 : 4;
+  if (const char* r = std::getenv("GCA_SPLIT_RATIO")) {  // tuning: split size ratio, <= 1 disables
+    float v = std::strtof(r, nullptr);
+    if (v > 0.f && v < 16.f) c->split_ratio = v;
+  }
   size_t page_elems = (size_t)g.H * g.P * g.D;
   // pages [0, N) are handed out by the ring; page N stays zero forever and
   // pads the gather list
