@@ -161,13 +161,23 @@ __global__ __launch_bounds__(256) void k_append(AppendArgs a) {
 // pushed positions [ring_tail, ring_tail + ppf) never overlap modulo N because
 // the evicted frame's own pages are live while it is evicted.
 
+// Workgroup b of an eviction: head h = b / evict_groups(C), compact tokens
+// [4g, 4g + 4) with g = b % evict_groups(C), one (token, dim) element per
+// thread, so every element's chain of dependent loads (compact offset, source
+// page, element) runs in parallel.  Group 0 of each head also zeroes its last
+// trajectory page past the new end; group 0 of head 0 records the popped
+// trajectory pages and pushes the evicted frame's pages to the ring tail.
+__host__ __device__ inline int evict_groups(int C) { return C > 4 ? (C + 3) / 4 : 1; }
+
 template <typename T>
-__device__ inline void evict_block(const EvictArgs& a, int h) {
+__device__ inline void evict_block(const EvictArgs& a, int b) {
   const int tid = threadIdx.x;
+  const int ng = evict_groups(a.C);
+  const int h = b / ng, grp = b % ng;
   T* kp = (T*)a.kpool;
   T* vp = (T*)a.vpool;
-  for (int idx = tid; idx < a.C * kHeadDim; idx += 256) {
-    int j = idx / kHeadDim, d = idx - j * kHeadDim;
+  const int j = grp * 4 + (tid >> 6), d = tid & 63;
+  if (j < a.C) {
     int tok = a.compact[j];
     int src = a.rec_pages[a.slot * a.ppf + tok / a.P];
     int ss = tok % a.P;
@@ -181,6 +191,7 @@ __device__ inline void evict_block(const EvictArgs& a, int h) {
     vp[(((size_t)dst * a.H + h) * kHeadDim + d) * a.P + ds] =
         vp[(((size_t)src * a.H + h) * kHeadDim + d) * a.P + ss];
   }
+  if (grp != 0) return;
   // slots of the last written trajectory page past the new end stay zero (a
   // popped page holds stale data); they are disjoint from the slots copied above
   const int64_t end = a.traj_len + a.C;
@@ -191,9 +202,9 @@ __device__ inline void evict_block(const EvictArgs& a, int h) {
                                   : a.ring[(a.ring_head + (pi - a.n_traj_pages)) % a.N];
     const int n = (a.P - fill) * kHeadDim;
     for (int idx = tid; idx < n; idx += 256) {
-      int j = idx / kHeadDim, d = idx - j * kHeadDim;
-      kp[(((size_t)dst * a.H + h) * a.P + fill + j) * kHeadDim + d] = from_f<T>(0.f);
-      vp[(((size_t)dst * a.H + h) * kHeadDim + d) * a.P + fill + j] = from_f<T>(0.f);
+      int jj = idx / kHeadDim, dd = idx - jj * kHeadDim;
+      kp[(((size_t)dst * a.H + h) * a.P + fill + jj) * kHeadDim + dd] = from_f<T>(0.f);
+      vp[(((size_t)dst * a.H + h) * kHeadDim + dd) * a.P + fill + jj] = from_f<T>(0.f);
     }
   }
   if (h == 0) {
@@ -250,7 +261,7 @@ __global__ __launch_bounds__(256) void k_prepare(SelectArgs sa, RopeArgs ra, int
 }
 
 // The per-frame update as one launch.  Block ranges: [0, na) append blocks
-// (page i = b % ppf, head b / ppf), [na, na + ne) eviction blocks (head),
+// (page i = b % ppf, head b / ppf), [na, na + ne) eviction blocks (head, token group),
 // [.., + nr) query rotation chunks, [.., + ns) gather-list entries.  The
 // append writes the new frame's pages and record slot; the eviction reads
 // the oldest window frame's pages, writes trajectory pages popped after the
@@ -781,7 +792,7 @@ hipError_t launch_append(int dtype, const AppendArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_evict(int dtype, const EvictArgs& a, hipStream_t s) {
-  dim3 grid(a.H);
+  dim3 grid(a.H * evict_groups(a.C));
   if (dtype) hipLaunchKernelGGL(k_evict<bf16>, grid, dim3(256), 0, s, a);
   else hipLaunchKernelGGL(k_evict<float>, grid, dim3(256), 0, s, a);
   return hipGetLastError();
@@ -800,7 +811,7 @@ hipError_t launch_update(int dtype, const AppendArgs* ap, const EvictArgs* ev, c
   RopeArgs r0{};
   SelectArgs s0{};
   const int na = ap ? ap->ppf * ap->H : 0;
-  const int ne = ev ? ev->H : 0;
+  const int ne = ev ? ev->H * evict_groups(ev->C) : 0;
   const int nr = ra ? (int)(((dtype ? rope_chunks<bf16>(*ra) : rope_chunks<float>(*ra)) + 255) / 256) : 0;
   const int ns = sa ? (sa->n_write + 255) / 256 : 0;
   const int nb = na + ne + nr + ns;
