@@ -749,26 +749,33 @@ __global__ __launch_bounds__(256) void k_merge(MergeArgs a) {
   int row = blockIdx.x * 16 + (threadIdx.x >> 4);
   int d = (threadIdx.x & 15) * 4;
   if (row >= a.rows) return;
+  // every split's lse and partial are loaded at once (one memory round
+  // trip); an empty split (lse = -inf, partial 0) gets weight 0
   float ls[kMaxSplitsDev];
+  floatx4 v[kMaxSplitsDev];
   float mx = -INFINITY;
 #pragma unroll
   for (int s = 0; s < kMaxSplitsDev; ++s) {
-    ls[s] = s < a.S ? a.lse_part[(size_t)s * a.rows + row] : -INFINITY;
-    mx = fmaxf(mx, ls[s]);
+    if (s < a.S) {
+      ls[s] = a.lse_part[(size_t)s * a.rows + row];
+      v[s] = *(const floatx4*)(a.o_part + ((size_t)s * a.rows + row) * kHeadDim + d);
+    } else {
+      ls[s] = -INFINITY;
+      v[s] = floatx4{0.f, 0.f, 0.f, 0.f};
+    }
   }
+#pragma unroll
+  for (int s = 0; s < kMaxSplitsDev; ++s) mx = fmaxf(mx, ls[s]);
   floatx4 acc = {0.f, 0.f, 0.f, 0.f};
   float sum = 0.f;
 #pragma unroll
   for (int s = 0; s < kMaxSplitsDev; ++s) {
-    if (s < a.S && ls[s] != -INFINITY) {
-      float w = __expf(ls[s] - mx);
-      floatx4 v = *(const floatx4*)(a.o_part + ((size_t)s * a.rows + row) * kHeadDim + d);
-      sum += w;
-      acc[0] = __builtin_fmaf(w, v[0], acc[0]);
-      acc[1] = __builtin_fmaf(w, v[1], acc[1]);
-      acc[2] = __builtin_fmaf(w, v[2], acc[2]);
-      acc[3] = __builtin_fmaf(w, v[3], acc[3]);
-    }
+    const float w = ls[s] == -INFINITY ? 0.f : __expf(ls[s] - mx);
+    sum += w;
+    acc[0] = __builtin_fmaf(w, v[s][0], acc[0]);
+    acc[1] = __builtin_fmaf(w, v[s][1], acc[1]);
+    acc[2] = __builtin_fmaf(w, v[s][2], acc[2]);
+    acc[3] = __builtin_fmaf(w, v[s][3], acc[3]);
   }
   float inv = 1.f / sum;
   acc[0] *= inv; acc[1] *= inv; acc[2] *= inv; acc[3] *= inv;
