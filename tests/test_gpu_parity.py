@@ -144,6 +144,27 @@ def test_keep_every_token_and_window_never_full():
             _cmp_attention(p, f)
 
 
+@pytest.mark.parametrize("T,H,P,dtype,A,W,C,rope,ns,gh,gw,interval", [
+    (1, 1, 16, "f32", 1, 1, 1, 0, 0, 1, 1, 1),     # one token per frame, one head
+    (2, 3, 64, "bf16", 0, 2, 0, 1, 1, 1, 1, 2),    # one special + one patch token, no anchor, no trajectory
+    (17, 1, 16, "bf16", 2, 1, 17, 1, 2, 3, 5, 1),  # ragged page, C = T, window of one frame
+    (33, 5, 32, "f32", 1, 3, 4, 1, 0, 3, 11, 3),   # odd head count, TEMP frames
+])
+def test_degenerate_shapes(T, H, P, dtype, A, W, C, rope, ns, gh, gw, interval):
+    """Tiny and ragged frames: one token, one head, a single partial page per
+    frame, every token kept, odd head counts; every step against the oracle."""
+    w = WL.Workload(f"deg_T{T}_H{H}_P{P}", T=T, H=H, D=64, P=P, dtype=dtype, n_frames=7, A=A, W=W, C=C,
+                    rope=rope, num_special=ns, grid_h=gh, grid_w=gw, keyframe_interval=interval, seed=41)
+    p = Pair(w)
+    for f in range(w.n_frames):
+        key = p.step(f)
+        p.check_state()
+        _cmp_attention(p, f)
+        if not key:
+            p.rollback(f)
+            p.check_state()
+
+
 def _rows(T, n=48, seed=0):
     rng = np.random.default_rng(seed)
     fixed = [0, 1, 2, 3, 4, 5, 36, 37, 255, 256, 511, 512, 767, 768, 1000, T - 1]
