@@ -388,6 +388,28 @@ __device__ inline void load_q(const AttnArgs& a, int qbase, int h, int l32, int 
 }
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+typedef int32_t i32x2 __attribute__((ext_vector_type(2)));
+
+// N consecutive gather entries at a wave-uniform address, through the
+// constant address space: one scalar load (the list is not written during the
+// attention launch).  Entries past N read as 0.
+template <int N>
+__device__ inline i32x4 load_uniform(const int32_t* p) {
+  i32x4 v = {0, 0, 0, 0};
+  if constexpr (N == 4) {
+    v = *(const __attribute__((address_space(4))) i32x4*)(const void*)p;
+  } else if constexpr (N == 2) {
+    i32x2 u = *(const __attribute__((address_space(4))) i32x2*)(const void*)p;
+    v.x = u.x;
+    v.y = u.y;
+  } else {
+    v.x = *(const __attribute__((address_space(4))) int32_t*)(const void*)p;
+  }
+  return v;
+}
+__device__ inline int pick(i32x4 v, int j) { return j == 0 ? v.x : j == 1 ? v.y : j == 2 ? v.z : v.w; }
+
 template <typename T, int P>
 struct TileLoader {
   static constexpr int EPC = 16 / sizeof(T);           // elements per 16-byte chunk
@@ -412,8 +434,8 @@ struct TileLoader {
   uint32_t page_bytes;
   int pg_k[NC], pg_v;         // page ids of the next tile
   u32x4 kr[NC], vr[NC];       // 16-byte chunks of the next tile (native vectors: plain loads)
-  int len_me;                 // valid length of entry tid % EPT of the next tile
-  int dlen_me;                // the same for the tile held in kr / vr
+  i32x4 lens;                 // entry lengths of the tile whose page ids are held (uniform)
+  i32x4 dlens;                // the same for the tile held in kr / vr
 
   __device__ void init(const T* kpool, const T* vpool, int h, int H, int tid) {
     page_bytes = (uint32_t)(H * P * kHeadDim * sizeof(T));
@@ -422,28 +444,29 @@ struct TileLoader {
       kaddr[i] = (const char*)(kpool + ((h * P) + (k_row(tid, i) % P)) * kHeadDim + k_part(tid) * EPC);
     vaddr = (const char*)(vpool + (h * kHeadDim + v_row(tid, 0)) * P + (v_key0(tid) % P));
   }
-  // page ids (and lengths) of tile `tile`; the gather list is padded past its end
+  // page ids and lengths of tile `tile` (scalar loads; the gather list is
+  // padded past its end); each thread picks the entries of its chunks
   __device__ void fetch_pages(const AttnArgs& a, int tile, int tid) {
+    const i32x4 pg = load_uniform<EPT>(a.sel_page + tile * EPT);
+    lens = load_uniform<EPT>(a.sel_len + tile * EPT);
 #pragma unroll
-    for (int i = 0; i < NC; ++i) pg_k[i] = a.sel_page[tile * EPT + k_row(tid, i) / P];
-    pg_v = a.sel_page[tile * EPT + v_key0(tid) / P];
-    len_me = a.sel_len[tile * EPT + tid % EPT];
+    for (int i = 0; i < NC; ++i) pg_k[i] = pick(pg, k_row(tid, i) / P);
+    pg_v = pick(pg, v_key0(tid) / P);
   }
   __device__ void fetch_data(int tid) {
-    dlen_me = len_me;
+    dlens = lens;
 #pragma unroll
     for (int i = 0; i < NC; ++i) {
       kr[i] = *(const u32x4*)(kaddr[i] + (uint64_t)(uint32_t)pg_k[i] * page_bytes);
       vr[i] = *(const u32x4*)(vaddr + (uint64_t)(uint32_t)pg_v * page_bytes + i * VSTEP);
     }
   }
-  __device__ void store(T* tileb, int* llen, int tid) {
+  __device__ void store(T* tileb, int tid) {
 #pragma unroll
     for (int i = 0; i < NC; ++i) {
       *(u32x4*)(tileb + k_row(tid, i) * KP + k_part(tid) * EPC) = kr[i];
       *(u32x4*)(tileb + kKeysPerTile * KP + v_row(tid, i) * VP + v_key0(tid)) = vr[i];
     }
-    if (tid < EPT) llen[tid] = dlen_me;
   }
 };
 
@@ -483,7 +506,6 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
   constexpr int EPT = L::EPT;
   constexpr int QPW = NQB * 32;              // queries per wave
   __shared__ __attribute__((aligned(16))) T lt[2][L::TILE_ELEMS];  // double-buffered tiles
-  __shared__ __attribute__((aligned(16))) int llen[2][4];
   // bf16: each wave's rotated query fragments wait in LDS in operand order
   // [qb][dc][lane] (conflict-free 16-byte reads), freeing 32 VGPRs so LDS
   // operand reads can be issued well ahead of their MFMAs.
@@ -557,7 +579,8 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
   } else {
     load_q(a, qbase, h, l32, hi, qf);
   }
-  if (t0 < t1) ld.store(lt[t0 & 1], llen[t0 & 1], tid);
+  if (t0 < t1) ld.store(lt[t0 & 1], tid);
+  i32x4 cur_lens = ld.dlens;  // entry lengths of the tile in LDS (uniform)
   __syncthreads();
 
   floatx16 o[2][NQB];
@@ -616,7 +639,7 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
     }
 
     // keys past a gather entry's valid length (partial pages) are masked
-    int4 lens = *(const int4*)llen[buf];
+    const i32x4 lens = cur_lens;
     bool full = lens.x == P;
     if (EPT > 1) full = full && lens.y == P;
     if (EPT > 2) full = full && lens.z == P && lens.w == P;
@@ -696,7 +719,8 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
         }
 
     // the other buffer was last read in the previous tile, before its barrier
-    if (more) ld.store(lt[buf ^ 1], llen[buf ^ 1], tid);
+    if (more) ld.store(lt[buf ^ 1], tid);
+    cur_lens = ld.dlens;
     __syncthreads();
   }
 
