@@ -506,10 +506,11 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
   constexpr int EPT = L::EPT;
   constexpr int QPW = NQB * 32;              // queries per wave
   __shared__ __attribute__((aligned(16))) T lt[2][L::TILE_ELEMS];  // double-buffered tiles
-  // bf16: each wave's rotated query fragments wait in LDS in operand order
-  // [qb][dc][lane] (conflict-free 16-byte reads), freeing 32 VGPRs so LDS
-  // operand reads can be issued well ahead of their MFMAs.
-  constexpr bool QLDS = sizeof(T) == 2;
+  // Query fragments stay in registers (B operands, 32 VGPRs) except for bf16
+  // with P = 64, whose loader needs more registers: there they wait in LDS in
+  // operand order [qb][dc][lane] (conflict-free 16-byte reads).  Measured:
+  // registers are faster at P = 16, LDS at P = 64.
+  constexpr bool QLDS = sizeof(T) == 2 && P == 64;
   __shared__ __attribute__((aligned(16))) Frag lq[QLDS ? kWaves * NQB * NDC * 64 : 1];
 
   // workgroup -> (head, split, q tile).  Dispatch is round-robin over the
