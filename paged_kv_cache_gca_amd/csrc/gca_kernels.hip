@@ -614,6 +614,32 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
 
     // S^T = K Q^T: s[kb][qb] holds keys kb*32 + 8*(r/4) + 4*hi + r%4 of query column l32
     floatx16 s[2][NQB];
+    if constexpr (!QLDS && sizeof(T) == 2) {
+      // the tile's 8 K fragments are read from LDS first, then the 16 MFMAs
+      // issue back to back instead of each pair waiting on its reads
+      Frag kf[2][NDC];
+#pragma unroll
+      for (int dc = 0; dc < NDC; ++dc)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) kf[kb][dc] = read_k(ck, L::KP, kb * 32 + l32, dc, hi);
+#pragma unroll
+      for (int dc = 0; dc < NDC; ++dc)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int qb = 0; qb < NQB; ++qb) {
+            if (dc == 0) {
+              floatx16 z;
+#pragma unroll
+              for (int r = 0; r < 16; ++r) z[r] = 0.f;
+              s[kb][qb] = M::mma(kf[kb][dc], qf[qb][dc], z);
+            } else {
+              s[kb][qb] = M::mma(kf[kb][dc], qf[qb][dc], s[kb][qb]);
+            }
+          }
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
+    } else
 #pragma unroll
     for (int dc = 0; dc < NDC; ++dc) {
       Frag qv[NQB];
