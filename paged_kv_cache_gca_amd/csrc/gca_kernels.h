@@ -81,7 +81,7 @@ struct SelectArgs {
 };
 
 struct AttnArgs {
-  const void* q;       // rotated [Tq][H][D]
+  const void* q;       // [Tq][H][D], rotated (3D RoPE) and scaled by sm_scale * log2(e)
   const void* kpool;   // [N][H][P][D]
   const void* vpool;   // [N][H][D][P]
   const int32_t* sel_page;
@@ -91,8 +91,6 @@ struct AttnArgs {
   void* out;           // [Tq][H][D] (S == 1)
   float* lse;          // [Tq][H] or null (S == 1)
   int64_t frame;
-  float sm_scale;      // > 0
-  float c2;            // sm_scale * log2(e)
   int Tq, H, P, n_sel, n_tiles, tiles_per_split, S, n_qtiles, n_units;
   int t_odd;           // > 0: even splits hold tiles_per_split tiles, odd ones t_odd
   int out_bf16;
@@ -114,6 +112,8 @@ struct RopeArgs {
   void* y;
   int64_t frame;
   int T, H;
+  int rotate;   // 0: y = scale * x (no rotation)
+  float scale;  // 1 for keys; sm_scale * log2(e) for the attention's queries
   RopeTabs tabs;
 };
 

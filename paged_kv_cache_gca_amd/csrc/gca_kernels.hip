@@ -65,21 +65,23 @@ __device__ inline void rotate(float x0, float x1, float2 cs, float& y0, float& y
   y1 = __builtin_fmaf(x0, cs.y, b);
 }
 
+// Rotated values times `scale` (exact for scale = 1), rounded once to T.
 template <typename T>
 __device__ inline void rotate_chunk(Vec16<T>& v, const RopeTabs& R, int64_t frame, int tok,
-                                    int first_pair) {
+                                    int first_pair, float scale = 1.f) {
   constexpr int EPC = 16 / sizeof(T);
 #pragma unroll
   for (int m = 0; m < EPC / 2; ++m) {
     float2 cs = rope_cs(R, frame, tok, first_pair + m);
     float y0, y1;
     rotate(to_f(v.e[2 * m]), to_f(v.e[2 * m + 1]), cs, y0, y1);
-    v.e[2 * m] = from_f<T>(y0);
-    v.e[2 * m + 1] = from_f<T>(y1);
+    v.e[2 * m] = from_f<T>(y0 * scale);
+    v.e[2 * m + 1] = from_f<T>(y1 * scale);
   }
 }
 
-// 16-byte chunk c of x -> y (rotated); chunks past the tensor are ignored
+// 16-byte chunk c of x -> y: rotated when a.rotate, times a.scale, rounded
+// once; chunks past the tensor are ignored
 template <typename T>
 __device__ inline void rope_chunk(const RopeArgs& a, size_t c) {
   constexpr int EPC = 16 / sizeof(T);
@@ -90,7 +92,12 @@ __device__ inline void rope_chunk(const RopeArgs& a, size_t c) {
   int tok = (int)(c / CPR / a.H);
   Vec16<T> v;
   v.u = ((const uint4*)a.x)[c];
-  rotate_chunk<T>(v, a.tabs, a.frame, tok, part * EPC / 2);
+  if (a.rotate) {
+    rotate_chunk<T>(v, a.tabs, a.frame, tok, part * EPC / 2, a.scale);
+  } else {
+#pragma unroll
+    for (int i = 0; i < EPC; ++i) v.e[i] = from_f<T>(to_f(v.e[i]) * a.scale);
+  }
   ((uint4*)a.y)[c] = v.u;
 }
 template <typename T>
@@ -310,23 +317,51 @@ __global__ void k_ring_init(int32_t* ring, const int32_t* init, int N) {
 
 template <typename T>
 struct Mfma;
+typedef short shortx4 __attribute__((ext_vector_type(4)));
+
+// Seed operands: a rank-1 product (A = ones in column 0, B = the value x of
+// each query column in row 0) fills a 32x32 accumulator with x per column.
+// Lanes with hi = 0 carry the k = 0 elements; the others are zero.
 template <>
 struct Mfma<bf16> {
   static constexpr int NQB = 2;  // 32-query blocks per wave
   static constexpr int KPL = 8;  // operand elements per lane
   typedef bf16x8 Frag;
+  typedef shortx4 Seed;
   __device__ static inline floatx16 mma(Frag a, Frag b, floatx16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
   }
+  __device__ static inline Seed seed(float x, int hi) {
+    Seed r = {0, 0, 0, 0};
+    if (hi == 0) r[0] = __builtin_bit_cast(short, (bf16)x);
+    return r;
+  }
+  __device__ static inline floatx16 mma_seed(Seed a, Seed b) {
+    floatx16 z;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) z[i] = 0.f;
+    return __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(a, b, z, 0, 0, 0);
+  }
+  // nearest value the seed operand holds exactly
+  __device__ static inline float exact(float x) { return (float)(bf16)x; }
 };
 template <>
 struct Mfma<float> {
   static constexpr int NQB = 1;
   static constexpr int KPL = 1;
   typedef float Frag;
+  typedef float Seed;
   __device__ static inline floatx16 mma(Frag a, Frag b, floatx16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
   }
+  __device__ static inline Seed seed(float x, int hi) { return hi == 0 ? x : 0.f; }
+  __device__ static inline floatx16 mma_seed(Seed a, Seed b) {
+    floatx16 z;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) z[i] = 0.f;
+    return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, z, 0, 0, 0);
+  }
+  __device__ static inline float exact(float x) { return x; }
 };
 
 // K operand: key row `row`, dims [dc*2*KPL + hi*KPL, +KPL).
@@ -338,15 +373,12 @@ __device__ inline float read_k(const float* lk, int pitch, int row, int dc, int 
 }
 
 // V^T operand for dim row d and chunk ch of key block kb: the keys whose S^T
-// accumulator registers form the matching P^T operand.
+// accumulator registers form the matching P^T operand, i.e. keys
+// 16*ch + 4*hi + {0..3} and 16*ch + 8 + 4*hi + {0..3} of the block.  The bf16
+// V^T tile holds each 16-key group in that order (keys 0-3, 8-11, 4-7,
+// 12-15), so the operand is one 16-byte read, laid out like the K reads.
 __device__ inline bf16x8 read_v(const bf16* lv, int pitch, int d, int kb, int ch, int hi) {
-  const bf16* p = lv + d * pitch + kb * 32 + ch * 16 + hi * 4;
-  bf16x4 x = *(const bf16x4*)p;
-  bf16x4 y = *(const bf16x4*)(p + 8);
-  bf16x8 r;
-  r[0] = x[0]; r[1] = x[1]; r[2] = x[2]; r[3] = x[3];
-  r[4] = y[0]; r[5] = y[1]; r[6] = y[2]; r[7] = y[3];
-  return r;
+  return *(const bf16x8*)(lv + d * pitch + kb * 32 + ch * 16 + hi * 8);
 }
 __device__ inline float read_v(const float* lv, int pitch, int d, int kb, int ch, int hi) {
   return lv[d * pitch + kb * 32 + (ch >> 2) * 8 + hi * 4 + (ch & 3)];
@@ -388,6 +420,7 @@ __device__ inline void load_q(const AttnArgs& a, int qbase, int h, int l32, int 
 }
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 typedef int32_t i32x2 __attribute__((ext_vector_type(2)));
 
@@ -465,7 +498,17 @@ struct TileLoader {
 #pragma unroll
     for (int i = 0; i < NC; ++i) {
       *(u32x4*)(tileb + k_row(tid, i) * KP + k_part(tid) * EPC) = kr[i];
-      *(u32x4*)(tileb + kKeysPerTile * KP + v_row(tid, i) * VP + v_key0(tid)) = vr[i];
+      T* vrow = tileb + kKeysPerTile * KP + v_row(tid, i) * VP;
+      if constexpr (sizeof(T) == 2) {
+        // keys 8j..8j+7: the first four go to 16*(j/2) + 4*(j%2), the
+        // other four 8 elements further (the operand order of read_v)
+        const int j = v_key0(tid) / 8;
+        T* dst = vrow + (j >> 1) * 16 + (j & 1) * 4;
+        *(u32x2*)dst = vr[i].xy;
+        *(u32x2*)(dst + 8) = vr[i].zw;
+      } else {
+        *(u32x4*)(vrow + v_key0(tid)) = vr[i];
+      }
     }
   }
 };
@@ -591,16 +634,25 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
     for (int j = 0; j < NQB; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) o[i][j][r] = 0.f;
+  // Scores are in log2 units: the queries arrive scaled by sm_scale*log2(e).
+  // m is each query column's running max offset, a value the seed operand
+  // holds exactly; every tile's S^T accumulators start at -m (a rank-1 MFMA,
+  // ones x -m), so P = exp2(S^T) directly.  m is raised lazily: a tile is
+  // accepted while the sum of each lane's P stays <= 2^16 (then no P
+  // exceeds 2^16 and nothing can overflow); otherwise (the first tile, or a
+  // max that rose by more than 16) the tile is redone from its raw scores
+  // with m raised to the tile max where that exceeds m by more than 8.
   float m[NQB], l[NQB];
+  const typename M::Seed ones = M::seed(1.f, hi);
+  typename M::Seed nm[NQB];
 #pragma unroll
   for (int qb = 0; qb < NQB; ++qb) {
     m[qb] = -INFINITY;
     l[qb] = 0.f;
+    nm[qb] = M::seed(INFINITY, hi);
   }
-  const float c2 = a.c2;
-  // The running max is only raised when a tile's max exceeds it by more than
-  // 2^8 in exp2 units; below that, exp2 stays <= 256, exact enough in fp32/bf16.
-  const float thr = 8.0f / c2;
+  constexpr float kMaxTileSum = 65536.f;
+  constexpr float kRaise = 8.f;
 
   for (int tile = t0; tile < t1; ++tile) {
     const int buf = tile & 1;
@@ -612,126 +664,132 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
     const T* ck = lt[buf];
     const T* cv = lt[buf] + kKeysPerTile * L::KP;
 
-    // S^T = K Q^T: s[kb][qb] holds keys kb*32 + 8*(r/4) + 4*hi + r%4 of query column l32
-    floatx16 s[2][NQB];
-    if constexpr (!QLDS && sizeof(T) == 2) {
-      // the tile's 8 K fragments are read from LDS first, then the 16 MFMAs
-      // issue back to back instead of each pair waiting on its reads
-      Frag kf[2][NDC];
+    // S^T = init + K Q^T: s[kb][qb] holds keys kb*32 + 8*(r/4) + 4*hi + r%4 of
+    // query column l32; init[qb] is the same for both key blocks
+    auto qk = [&](floatx16 (&s)[2][NQB], const floatx16 (&init)[NQB]) {
+      if constexpr (!QLDS && sizeof(T) == 2) {
+        // the tile's 8 K fragments are read from LDS first, then the MFMAs
+        // issue back to back instead of each pair waiting on its reads
+        Frag kf[2][NDC];
 #pragma unroll
-      for (int dc = 0; dc < NDC; ++dc)
+        for (int dc = 0; dc < NDC; ++dc)
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) kf[kb][dc] = read_k(ck, L::KP, kb * 32 + l32, dc, hi);
+          for (int kb = 0; kb < 2; ++kb) kf[kb][dc] = read_k(ck, L::KP, kb * 32 + l32, dc, hi);
 #pragma unroll
-      for (int dc = 0; dc < NDC; ++dc)
+        for (int dc = 0; dc < NDC; ++dc)
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int qb = 0; qb < NQB; ++qb)
+              s[kb][qb] = M::mma(kf[kb][dc], qf[qb][dc], dc == 0 ? init[qb] : s[kb][qb]);
+        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
+      } else {
+#pragma unroll
+        for (int dc = 0; dc < NDC; ++dc) {
+          Frag qv[NQB];
+#pragma unroll
+          for (int qb = 0; qb < NQB; ++qb) {
+            if constexpr (QLDS) qv[qb] = mq[(qb * NDC + dc) * 64 + lane];
+            else qv[qb] = qf[qb][dc];
+          }
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb) {
+            Frag kf = read_k(ck, L::KP, kb * 32 + l32, dc, hi);
+#pragma unroll
+            for (int qb = 0; qb < NQB; ++qb)
+              s[kb][qb] = M::mma(kf, qv[qb], dc == 0 ? init[qb] : s[kb][qb]);
+          }
+        }
+      }
+      // keys past a gather entry's valid length (partial pages) are masked
+      const i32x4 lens = cur_lens;
+      bool full = lens.x == P;
+      if (EPT > 1) full = full && lens.y == P;
+      if (EPT > 2) full = full && lens.z == P && lens.w == P;
+      if (__builtin_expect(!full, 0)) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int qb = 0; qb < NQB; ++qb) {
-            if (dc == 0) {
-              floatx16 z;
+          for (int r = 0; r < 16; ++r) {
+            // key kb*32 + 8*(r/4) + 4*hi + r%4: P is a multiple of 8, so its
+            // entry is known at compile time and only the slot depends on hi
+            const int k8 = kb * 32 + (r >> 2) * 8;
+            const int e = k8 / P;
+            const int len = e == 0 ? lens.x : e == 1 ? lens.y : e == 2 ? lens.z : lens.w;
+            if ((k8 % P) + hi * 4 + (r & 3) >= len) {
 #pragma unroll
-              for (int r = 0; r < 16; ++r) z[r] = 0.f;
-              s[kb][qb] = M::mma(kf[kb][dc], qf[qb][dc], z);
-            } else {
-              s[kb][qb] = M::mma(kf[kb][dc], qf[qb][dc], s[kb][qb]);
+              for (int qb = 0; qb < NQB; ++qb) s[kb][qb][r] = -INFINITY;
             }
           }
-      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
-    } else
-#pragma unroll
-    for (int dc = 0; dc < NDC; ++dc) {
-      Frag qv[NQB];
+      }
+    };
+    // P = exp2(S^T) rounded to the MFMA operand type; this lane's sums of the same P
+    auto expsum = [&](floatx16 (&s)[2][NQB], Frag (&pf)[2][NCH][NQB], float (&ts)[NQB]) {
 #pragma unroll
       for (int qb = 0; qb < NQB; ++qb) {
-        if constexpr (QLDS) qv[qb] = mq[(qb * NDC + dc) * 64 + lane];
-        else qv[qb] = qf[qb][dc];
-      }
+        ts[qb] = 0.f;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        Frag kf = read_k(ck, L::KP, kb * 32 + l32, dc, hi);
+        for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-        for (int qb = 0; qb < NQB; ++qb) {
-          if (dc == 0) {
-            floatx16 z;
+          for (int r = 0; r < 16; ++r) s[kb][qb][r] = __builtin_amdgcn_exp2f(s[kb][qb][r]);
 #pragma unroll
-            for (int r = 0; r < 16; ++r) z[r] = 0.f;
-            s[kb][qb] = M::mma(kf, qv[qb], z);
-          } else {
-            s[kb][qb] = M::mma(kf, qv[qb], s[kb][qb]);
+          for (int ch = 0; ch < NCH; ++ch) {
+            pf[kb][ch][qb] = pack_p(s[kb][qb], ch, T());
+            ts[qb] = rowsum_add(ts[qb], pf[kb][ch][qb]);
           }
         }
       }
-    }
+    };
 
-    // keys past a gather entry's valid length (partial pages) are masked
-    const i32x4 lens = cur_lens;
-    bool full = lens.x == P;
-    if (EPT > 1) full = full && lens.y == P;
-    if (EPT > 2) full = full && lens.z == P && lens.w == P;
-    if (!full) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          // key kb*32 + 8*(r/4) + 4*hi + r%4: P is a multiple of 8, so its
-          // entry is known at compile time and only the slot depends on hi
-          const int k8 = kb * 32 + (r >> 2) * 8;
-          const int e = k8 / P;
-          const int len = e == 0 ? lens.x : e == 1 ? lens.y : e == 2 ? lens.z : lens.w;
-          if ((k8 % P) + hi * 4 + (r & 3) >= len) {
-#pragma unroll
-            for (int qb = 0; qb < NQB; ++qb) s[kb][qb][r] = -INFINITY;
-          }
-        }
-    }
-
-    // running max per query column (one column per lane); raise it only when
-    // the tile exceeds it by the threshold
-    bool raise[NQB];
-    float mx[NQB];
-    bool any = false;
-#pragma unroll
-    for (int qb = 0; qb < NQB; ++qb) {
-      float x = s[0][qb][0];
-#pragma unroll
-      for (int r = 1; r < 16; ++r) x = fmaxf(x, s[0][qb][r]);
-#pragma unroll
-      for (int r = 0; r < 16; ++r) x = fmaxf(x, s[1][qb][r]);
-      mx[qb] = half_swap_max(x);
-      raise[qb] = mx[qb] > m[qb] + thr;
-      any = any || raise[qb];
-    }
-    if (__any(any)) {
-#pragma unroll
-      for (int qb = 0; qb < NQB; ++qb) {
-        float mn = raise[qb] ? mx[qb] : m[qb];
-        float alpha = __builtin_amdgcn_exp2f((m[qb] - mn) * c2);
-        m[qb] = mn;
-        o[0][qb] *= alpha;
-        o[1][qb] *= alpha;
-        l[qb] *= alpha;
-      }
-    }
-
-    // P = exp2(S - m) rounded to the MFMA operand type; row sums of the same P
+    floatx16 s[2][NQB];
     Frag pf[2][NCH][NQB];
+    float ts[NQB];
+    {
+      floatx16 init[NQB];
 #pragma unroll
-    for (int qb = 0; qb < NQB; ++qb) {
-      float mc = m[qb] * c2;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          s[kb][qb][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][qb][r], c2, -mc));
-#pragma unroll
-        for (int ch = 0; ch < NCH; ++ch) {
-          pf[kb][ch][qb] = pack_p(s[kb][qb], ch, T());
-          l[qb] = rowsum_add(l[qb], pf[kb][ch][qb]);
-        }
-      }
+      for (int qb = 0; qb < NQB; ++qb) init[qb] = M::mma_seed(ones, nm[qb]);
+      qk(s, init);
     }
+    expsum(s, pf, ts);
+    bool redo = false;
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) redo = redo || !(ts[qb] <= kMaxTileSum);
+    if (__any(redo)) {
+      floatx16 init[NQB];
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) init[qb][r] = 0.f;
+      qk(s, init);
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) {
+        float x = s[0][qb][0];
+#pragma unroll
+        for (int r = 1; r < 16; ++r) x = fmaxf(x, s[0][qb][r]);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) x = fmaxf(x, s[1][qb][r]);
+        const float mx = half_swap_max(x);
+        if (mx > m[qb] + kRaise) {
+          const float mn = M::exact(mx);
+          const float alpha = __builtin_amdgcn_exp2f(m[qb] - mn);  // 0 while m = -inf
+          m[qb] = mn;
+          nm[qb] = M::seed(-mn, hi);
+          o[0][qb] *= alpha;
+          o[1][qb] *= alpha;
+          l[qb] *= alpha;
+        }
+        // a column with no valid key so far keeps m = -inf: its P is 0
+        const float off = m[qb] == -INFINITY ? 0.f : m[qb];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) s[kb][qb][r] -= off;
+      }
+      expsum(s, pf, ts);
+    }
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) l[qb] += ts[qb];
 
     // O^T += V^T P^T
 #pragma unroll
@@ -763,7 +821,7 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
     if (q >= a.Tq) continue;
     bool empty = !(l[qb] > 0.f);
     float inv = empty ? 0.f : 1.f / l[qb];
-    float lse = empty ? -INFINITY : m[qb] * a.sm_scale + __logf(l[qb]);
+    float lse = empty ? -INFINITY : m[qb] * 0.69314718f + __logf(l[qb]);  // m is in log2 units
     size_t row = (size_t)q * a.H + h;
 #pragma unroll
     for (int db = 0; db < 2; ++db)

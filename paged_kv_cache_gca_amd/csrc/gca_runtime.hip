@@ -66,7 +66,7 @@ struct gca_cache {
   gca::RopeTabs tabs{};
   float* o_part = nullptr;
   float* lse_part = nullptr;
-  void* qrot = nullptr;  // rotated queries of the current attention call
+  void* qrot = nullptr;  // prepared queries (rotated, scaled) of the current attention call
   // tiles of a first-dispatched split per tile of a second-dispatched one
   float split_ratio = 1.7f;
   bool sel_valid = false;
@@ -221,19 +221,23 @@ gca::EvictArgs evict_args(gca_cache* c, const gca::EvictStep& st) {
   return a;
 }
 
-gca::RopeArgs rope_args(gca_cache* c, int64_t frame_idx, const void* x, void* y) {
+// The attention's queries: rotated when rope = 1 and scaled by
+// sm_scale * log2(e), rounded once, into the query workspace.
+gca::RopeArgs query_args(gca_cache* c, int64_t frame_idx, const void* q) {
   gca::RopeArgs ra;
-  ra.x = x;
-  ra.y = y;
+  ra.x = q;
+  ra.y = c->qrot;
   ra.frame = frame_idx;
   ra.T = c->g.T;
   ra.H = c->g.H;
+  ra.rotate = c->g.rope;
+  ra.scale = (float)((double)c->g.scale * 1.4426950408889634);
   ra.tabs = c->tabs;
   return ra;
 }
 
 // Attention over the gather list already built for `st` (queries qa already
-// rotated when rope = 1), then the split merge.
+// prepared by query_args), then the split merge.
 int attend_launch(gca_cache* c, int64_t frame_idx, const void* qa, void* out, float* lse,
                   const gca::SelectStep& st, hipStream_t s) {
   const gca::Geometry& g = c->g;
@@ -260,8 +264,6 @@ int attend_launch(gca_cache* c, int64_t frame_idx, const void* qa, void* out, fl
   a.out = out;
   a.lse = lse;
   a.frame = frame_idx;
-  a.sm_scale = g.scale;
-  a.c2 = (float)((double)g.scale * 1.4426950408889634);
   a.Tq = g.T;
   a.H = g.H;
   a.P = g.P;
@@ -369,7 +371,7 @@ int gca_cache_create(const gca_config* cfg, gca_cache** out) {
     return fail(e, "hipMalloc split workspace");
   if ((e = dmalloc(&c->lse_part, sizeof(float) * rows * kMaxSplits)) != hipSuccess)
     return fail(e, "hipMalloc split workspace");
-  if (g.rope && (e = dmalloc(&c->qrot, rows * g.D * c->esize)) != hipSuccess)
+  if ((e = dmalloc(&c->qrot, rows * g.D * c->esize)) != hipSuccess)
     return fail(e, "hipMalloc query workspace");
   if ((e = hipMemset(c->kpool, 0, pool_bytes)) != hipSuccess) return fail(e, "hipMemset K pool");
   if ((e = hipMemset(c->vpool, 0, pool_bytes)) != hipSuccess) return fail(e, "hipMemset V pool");
@@ -482,21 +484,16 @@ int gca_attend(gca_cache* c, int64_t frame_idx, const void* q, void* out, float*
   hipStream_t s = (hipStream_t)stream;
   const gca::Geometry& g = c->g;
   gca::SelectStep st = c->plan.select();
-  const void* qa = q;
-  if (g.rope) {
-    // gather list and rotated queries from one launch
-    gca::RopeArgs ra = rope_args(c, frame_idx, q, c->qrot);
+  {
+    // gather list and prepared queries from one launch
     Prof p(c, 2, s);
-    GCA_HIP(gca::launch_prepare(g.dtype, select_args(c, st), ra, s), "prepare kernel launch");
-    qa = c->qrot;
-  } else {
-    Prof p(c, 2, s);
-    GCA_HIP(gca::launch_select(select_args(c, st), s), "select kernel launch");
+    GCA_HIP(gca::launch_prepare(g.dtype, select_args(c, st), query_args(c, frame_idx, q), s),
+            "prepare kernel launch");
   }
   c->sel_valid = true;
   c->sel_n = st.n_sel;
   c->sel_ctx = st.n_ctx;
-  return attend_launch(c, frame_idx, qa, out, lse, st, s);
+  return attend_launch(c, frame_idx, c->qrot, out, lse, st, s);
 }
 
 int gca_rollback_last_frame(gca_cache* c, int64_t frame_idx, gca_stream_t stream) {
@@ -544,7 +541,7 @@ int gca_step(gca_cache* c, int64_t frame_idx, const void* k, const void* v, cons
   gca::AppendArgs aa = append_args(c, as, k, v);
   gca::EvictArgs ea{};
   if (!ev.empty()) ea = evict_args(c, ev[0]);
-  gca::RopeArgs ra = rope_args(c, frame_idx, q, c->qrot);
+  gca::RopeArgs ra = query_args(c, frame_idx, q);
   gca::SelectArgs sa = select_args(c, st);
   sa.newest_pos = as.ring_pos % g.N;
   if (!ev.empty()) {
@@ -553,14 +550,14 @@ int gca_step(gca_cache* c, int64_t frame_idx, const void* k, const void* v, cons
   }
   {
     Prof pr(c, 6, s);
-    GCA_HIP(gca::launch_update(g.dtype, &aa, ev.empty() ? nullptr : &ea, g.rope ? &ra : nullptr, &sa, s),
+    GCA_HIP(gca::launch_update(g.dtype, &aa, ev.empty() ? nullptr : &ea, &ra, &sa, s),
             "update kernel launch");
   }
   c->plan = p;
   c->sel_valid = true;
   c->sel_n = st.n_sel;
   c->sel_ctx = st.n_ctx;
-  rc = attend_launch(c, frame_idx, g.rope ? (const void*)c->qrot : q, out, lse, st, s);
+  rc = attend_launch(c, frame_idx, c->qrot, out, lse, st, s);
   if (rc) return rc;
   if (!key) {
     c->plan.commit_rollback();
@@ -580,6 +577,8 @@ int gca_rope3d(gca_cache* c, int64_t frame_idx, const void* x, void* y, gca_stre
   a.frame = frame_idx;
   a.T = c->g.T;
   a.H = c->g.H;
+  a.rotate = 1;
+  a.scale = 1.f;
   a.tabs = c->tabs;
   Prof p(c, 5, s);
   GCA_HIP(gca::launch_rope(c->g.dtype, a, s), "rope kernel launch");
