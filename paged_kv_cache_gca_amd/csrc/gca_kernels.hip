@@ -319,21 +319,37 @@ template <typename T>
 struct Mfma;
 typedef short shortx4 __attribute__((ext_vector_type(4)));
 
-// Seed operands: a rank-1 product (A = ones in column 0, B = the value x of
-// each query column in row 0) fills a 32x32 accumulator with x per column.
-// Lanes with hi = 0 carry the k = 0 elements; the others are zero.
+// Seed operands: a rank-2 product fills a 32x32 S^T accumulator before the
+// K.Q^T MFMAs.  A holds, per key row, 1 in column 0 and the key's mask (1 for
+// a key past its page's valid length, else 0) in column 1; B holds, per query
+// column, the offset x in row 0 and -1e30 in row 1.  The product is x for a
+// valid key and x - 1e30 (exp2 of which is 0) for a masked one.
+constexpr float kMaskedScore = -1e30f;
+
 template <>
 struct Mfma<bf16> {
   static constexpr int NQB = 2;  // 32-query blocks per wave
   static constexpr int KPL = 8;  // operand elements per lane
   typedef bf16x8 Frag;
-  typedef shortx4 Seed;
+  typedef shortx4 Seed;          // 32x32x8 operand: lane (l32, hi) holds k = 4*hi .. 4*hi+3
   __device__ static inline floatx16 mma(Frag a, Frag b, floatx16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
   }
-  __device__ static inline Seed seed(float x, int hi) {
+  __device__ static inline short bits(float x) { return __builtin_bit_cast(short, (bf16)x); }
+  __device__ static inline Seed seed_a(float mask, int hi) {
     Seed r = {0, 0, 0, 0};
-    if (hi == 0) r[0] = __builtin_bit_cast(short, (bf16)x);
+    if (hi == 0) {
+      r[0] = bits(1.f);
+      r[1] = bits(mask);
+    }
+    return r;
+  }
+  __device__ static inline Seed seed_b(float x, int hi) {
+    Seed r = {0, 0, 0, 0};
+    if (hi == 0) {
+      r[0] = bits(x);
+      r[1] = bits(kMaskedScore);
+    }
     return r;
   }
   __device__ static inline floatx16 mma_seed(Seed a, Seed b) {
@@ -350,11 +366,12 @@ struct Mfma<float> {
   static constexpr int NQB = 1;
   static constexpr int KPL = 1;
   typedef float Frag;
-  typedef float Seed;
+  typedef float Seed;            // 32x32x2 operand: lane (l32, hi) holds k = hi
   __device__ static inline floatx16 mma(Frag a, Frag b, floatx16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
   }
-  __device__ static inline Seed seed(float x, int hi) { return hi == 0 ? x : 0.f; }
+  __device__ static inline Seed seed_a(float mask, int hi) { return hi == 0 ? 1.f : mask; }
+  __device__ static inline Seed seed_b(float x, int hi) { return hi == 0 ? x : kMaskedScore; }
   __device__ static inline floatx16 mma_seed(Seed a, Seed b) {
     floatx16 z;
 #pragma unroll
@@ -424,25 +441,6 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 typedef int32_t i32x2 __attribute__((ext_vector_type(2)));
 
-// N consecutive gather entries at a wave-uniform address, through the
-// constant address space: one scalar load (the list is not written during the
-// attention launch).  Entries past N read as 0.
-template <int N>
-__device__ inline i32x4 load_uniform(const int32_t* p) {
-  i32x4 v = {0, 0, 0, 0};
-  if constexpr (N == 4) {
-    v = *(const __attribute__((address_space(4))) i32x4*)(const void*)p;
-  } else if constexpr (N == 2) {
-    i32x2 u = *(const __attribute__((address_space(4))) i32x2*)(const void*)p;
-    v.x = u.x;
-    v.y = u.y;
-  } else {
-    v.x = *(const __attribute__((address_space(4))) int32_t*)(const void*)p;
-  }
-  return v;
-}
-__device__ inline int pick(i32x4 v, int j) { return j == 0 ? v.x : j == 1 ? v.y : j == 2 ? v.z : v.w; }
-
 template <typename T, int P>
 struct TileLoader {
   static constexpr int EPC = 16 / sizeof(T);           // elements per 16-byte chunk
@@ -467,8 +465,9 @@ struct TileLoader {
   uint32_t page_bytes;
   int pg_k[NC], pg_v;         // page ids of the next tile
   u32x4 kr[NC], vr[NC];       // 16-byte chunks of the next tile (native vectors: plain loads)
-  i32x4 lens;                 // entry lengths of the tile whose page ids are held (uniform)
-  i32x4 dlens;                // the same for the tile held in kr / vr
+  int lens[2];                // valid lengths of the entries of keys l32 and 32 + l32 of the
+                              // tile whose page ids are held
+  int dlens[2];               // the same for the tile held in kr / vr
 
   __device__ void init(const T* kpool, const T* vpool, int h, int H, int tid) {
     page_bytes = (uint32_t)(H * P * kHeadDim * sizeof(T));
@@ -477,17 +476,35 @@ struct TileLoader {
       kaddr[i] = (const char*)(kpool + ((h * P) + (k_row(tid, i) % P)) * kHeadDim + k_part(tid) * EPC);
     vaddr = (const char*)(vpool + (h * kHeadDim + v_row(tid, 0)) * P + (v_key0(tid) % P));
   }
-  // page ids and lengths of tile `tile` (scalar loads; the gather list is
-  // padded past its end); each thread picks the entries of its chunks
+  // page ids and lengths of tile `tile` (the gather list is padded past its
+  // end).  With several entries per tile each thread loads those of its own
+  // chunks and keys with plain vector loads, consumed a whole tile later when
+  // that tile's data loads are issued; with one entry per tile (P = 64) a
+  // scalar load through the constant address space (the list is not written
+  // during the launch) serves the whole wave.
   __device__ void fetch_pages(const AttnArgs& a, int tile, int tid) {
-    const i32x4 pg = load_uniform<EPT>(a.sel_page + tile * EPT);
-    lens = load_uniform<EPT>(a.sel_len + tile * EPT);
+    if constexpr (EPT == 1) {
+      typedef const __attribute__((address_space(4))) int32_t cint;
+      const int pg = *(cint*)(const void*)(a.sel_page + tile);
+      const int ln = *(cint*)(const void*)(a.sel_len + tile);
 #pragma unroll
-    for (int i = 0; i < NC; ++i) pg_k[i] = pick(pg, k_row(tid, i) / P);
-    pg_v = pick(pg, v_key0(tid) / P);
+      for (int i = 0; i < NC; ++i) pg_k[i] = pg;
+      pg_v = pg;
+      lens[0] = ln;
+      lens[1] = ln;
+    } else {
+      const int32_t* sp = a.sel_page + tile * EPT;
+      const int32_t* sl = a.sel_len + tile * EPT;
+#pragma unroll
+      for (int i = 0; i < NC; ++i) pg_k[i] = sp[k_row(tid, i) / P];
+      pg_v = sp[v_key0(tid) / P];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) lens[kb] = sl[(kb * 32 + (tid & 31)) / P];
+    }
   }
   __device__ void fetch_data(int tid) {
-    dlens = lens;
+    dlens[0] = lens[0];
+    dlens[1] = lens[1];
 #pragma unroll
     for (int i = 0; i < NC; ++i) {
       kr[i] = *(const u32x4*)(kaddr[i] + (uint64_t)(uint32_t)pg_k[i] * page_bytes);
@@ -549,10 +566,10 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
   constexpr int EPT = L::EPT;
   constexpr int QPW = NQB * 32;              // queries per wave
   __shared__ __attribute__((aligned(16))) T lt[2][L::TILE_ELEMS];  // double-buffered tiles
-  // Query fragments stay in registers (B operands, 32 VGPRs) except for bf16
-  // with P = 64, whose loader needs more registers: there they wait in LDS in
-  // operand order [qb][dc][lane] (conflict-free 16-byte reads).  Measured:
-  // registers are faster at P = 16, LDS at P = 64.
+  // Query fragments stay in registers (B operands) except for bf16 with
+  // P = 64, where they wait in LDS in operand order [qb][dc][lane]
+  // (conflict-free 16-byte reads) and each tile runs as one block (measured
+  // faster there; at P = 16 and 32 registers and the two-block pipeline are).
   constexpr bool QLDS = sizeof(T) == 2 && P == 64;
   __shared__ __attribute__((aligned(16))) Frag lq[QLDS ? kWaves * NQB * NDC * 64 : 1];
 
@@ -624,7 +641,7 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
     load_q(a, qbase, h, l32, hi, qf);
   }
   if (t0 < t1) ld.store(lt[t0 & 1], tid);
-  i32x4 cur_lens = ld.dlens;  // entry lengths of the tile in LDS (uniform)
+  int cur_lens[2] = {ld.dlens[0], ld.dlens[1]};  // entry lengths of the tile in LDS
   __syncthreads();
 
   floatx16 o[2][NQB];
@@ -635,23 +652,24 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) o[i][j][r] = 0.f;
   // Scores are in log2 units: the queries arrive scaled by sm_scale*log2(e).
-  // m is each query column's running max offset, a value the seed operand
-  // holds exactly; every tile's S^T accumulators start at -m (a rank-1 MFMA,
-  // ones x -m), so P = exp2(S^T) directly.  m is raised lazily: a tile is
-  // accepted while the sum of each lane's P stays <= 2^16 (then no P
-  // exceeds 2^16 and nothing can overflow); otherwise (the first tile, or a
-  // max that rose by more than 16) the tile is redone from its raw scores
-  // with m raised to the tile max where that exceeds m by more than 8.
+  // m is each query column's running offset, a value the seed operand holds
+  // exactly.  Every 32-key block's S^T accumulators start from the seed
+  // product, -m for a valid key and -m - 1e30 for a masked one, so
+  // P = exp2(S^T) directly and masked keys get P = 0.  m is raised lazily: a
+  // block is accepted while the sum of each lane's P over it stays <= 2^16
+  // (then no P exceeds 2^16 and nothing can overflow); otherwise (the first
+  // block, or a max that rose by more than 16) the block is redone from its
+  // raw scores, with m raised to the block max where that exceeds m by more
+  // than 8, and O and l rescaled.
   float m[NQB], l[NQB];
-  const typename M::Seed ones = M::seed(1.f, hi);
   typename M::Seed nm[NQB];
 #pragma unroll
   for (int qb = 0; qb < NQB; ++qb) {
     m[qb] = -INFINITY;
     l[qb] = 0.f;
-    nm[qb] = M::seed(INFINITY, hi);
+    nm[qb] = M::seed_b(INFINITY, hi);
   }
-  constexpr float kMaxTileSum = 65536.f;
+  constexpr float kMaxBlockSum = 65536.f;
   constexpr float kRaise = 8.f;
 
   for (int tile = t0; tile < t1; ++tile) {
@@ -664,117 +682,76 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
     const T* ck = lt[buf];
     const T* cv = lt[buf] + kKeysPerTile * L::KP;
 
-    // S^T = init + K Q^T: s[kb][qb] holds keys kb*32 + 8*(r/4) + 4*hi + r%4 of
-    // query column l32; init[qb] is the same for both key blocks
-    auto qk = [&](floatx16 (&s)[2][NQB], const floatx16 (&init)[NQB]) {
-      if constexpr (!QLDS && sizeof(T) == 2) {
-        // the tile's 8 K fragments are read from LDS first, then the MFMAs
-        // issue back to back instead of each pair waiting on its reads
-        Frag kf[2][NDC];
+    // seed A operands: key kb*32 + l32 is masked when past its gather
+    // entry's valid length (partial pages)
+    typename M::Seed sa[2];
 #pragma unroll
-        for (int dc = 0; dc < NDC; ++dc)
+    for (int kb = 0; kb < 2; ++kb) {
+      sa[kb] = M::seed_a((kb * 32 + l32) % P >= cur_lens[kb] ? 1.f : 0.f, hi);
+    }
+    // seed of key block kb: offset scores, or raw (offset 0) for a redo
+    auto seed = [&](int kb, bool raw, floatx16 (&init)[NQB]) {
 #pragma unroll
-          for (int kb = 0; kb < 2; ++kb) kf[kb][dc] = read_k(ck, L::KP, kb * 32 + l32, dc, hi);
+      for (int qb = 0; qb < NQB; ++qb) init[qb] = M::mma_seed(sa[kb], raw ? M::seed_b(0.f, hi) : nm[qb]);
+    };
+    // S^T of the whole tile (both key blocks): s[kb][qb] holds keys
+    // kb*32 + 8*(r/4) + 4*hi + r%4 of query column l32
+    auto qk_tile = [&](floatx16 (&s)[2][NQB], bool raw) {
+      seed(0, raw, s[0]);
+      seed(1, raw, s[1]);
 #pragma unroll
-        for (int dc = 0; dc < NDC; ++dc)
+      for (int dc = 0; dc < NDC; ++dc) {
+        Frag qv[NQB];
 #pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
+        for (int qb = 0; qb < NQB; ++qb) {
+          if constexpr (QLDS) qv[qb] = mq[(qb * NDC + dc) * 64 + lane];
+          else qv[qb] = qf[qb][dc];
+        }
 #pragma unroll
-            for (int qb = 0; qb < NQB; ++qb)
-              s[kb][qb] = M::mma(kf[kb][dc], qf[qb][dc], dc == 0 ? init[qb] : s[kb][qb]);
-        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
-      } else {
+        for (int kb = 0; kb < 2; ++kb) {
+          Frag kf = read_k(ck, L::KP, kb * 32 + l32, dc, hi);
 #pragma unroll
-        for (int dc = 0; dc < NDC; ++dc) {
-          Frag qv[NQB];
-#pragma unroll
-          for (int qb = 0; qb < NQB; ++qb) {
-            if constexpr (QLDS) qv[qb] = mq[(qb * NDC + dc) * 64 + lane];
-            else qv[qb] = qf[qb][dc];
-          }
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb) {
-            Frag kf = read_k(ck, L::KP, kb * 32 + l32, dc, hi);
-#pragma unroll
-            for (int qb = 0; qb < NQB; ++qb)
-              s[kb][qb] = M::mma(kf, qv[qb], dc == 0 ? init[qb] : s[kb][qb]);
-          }
+          for (int qb = 0; qb < NQB; ++qb) s[kb][qb] = M::mma(kf, qv[qb], s[kb][qb]);
         }
       }
-      // keys past a gather entry's valid length (partial pages) are masked
-      const i32x4 lens = cur_lens;
-      bool full = lens.x == P;
-      if (EPT > 1) full = full && lens.y == P;
-      if (EPT > 2) full = full && lens.z == P && lens.w == P;
-      if (__builtin_expect(!full, 0)) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            // key kb*32 + 8*(r/4) + 4*hi + r%4: P is a multiple of 8, so its
-            // entry is known at compile time and only the slot depends on hi
-            const int k8 = kb * 32 + (r >> 2) * 8;
-            const int e = k8 / P;
-            const int len = e == 0 ? lens.x : e == 1 ? lens.y : e == 2 ? lens.z : lens.w;
-            if ((k8 % P) + hi * 4 + (r & 3) >= len) {
-#pragma unroll
-              for (int qb = 0; qb < NQB; ++qb) s[kb][qb][r] = -INFINITY;
-            }
-          }
-      }
     };
-    // P = exp2(S^T) rounded to the MFMA operand type; this lane's sums of the same P
-    auto expsum = [&](floatx16 (&s)[2][NQB], Frag (&pf)[2][NCH][NQB], float (&ts)[NQB]) {
+    // exponentials, packing and this lane's sums of key block kb
+    auto exp_block = [&](int kb, floatx16 (&s)[2][NQB], Frag (&pf)[2][NCH][NQB], float (&ts)[NQB]) {
 #pragma unroll
       for (int qb = 0; qb < NQB; ++qb) {
         ts[qb] = 0.f;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
+        for (int r = 0; r < 16; ++r) s[kb][qb][r] = __builtin_amdgcn_exp2f(s[kb][qb][r]);
 #pragma unroll
-          for (int r = 0; r < 16; ++r) s[kb][qb][r] = __builtin_amdgcn_exp2f(s[kb][qb][r]);
-#pragma unroll
-          for (int ch = 0; ch < NCH; ++ch) {
-            pf[kb][ch][qb] = pack_p(s[kb][qb], ch, T());
-            ts[qb] = rowsum_add(ts[qb], pf[kb][ch][qb]);
-          }
+        for (int ch = 0; ch < NCH; ++ch) {
+          pf[kb][ch][qb] = pack_p(s[kb][qb], ch, T());
+          ts[qb] = rowsum_add(ts[qb], pf[kb][ch][qb]);
         }
       }
     };
-
-    floatx16 s[2][NQB];
-    Frag pf[2][NCH][NQB];
-    float ts[NQB];
-    {
-      floatx16 init[NQB];
+    auto sums_ok = [&](const float (&ts)[NQB]) {
+      bool bad = false;
 #pragma unroll
-      for (int qb = 0; qb < NQB; ++qb) init[qb] = M::mma_seed(ones, nm[qb]);
-      qk(s, init);
-    }
-    expsum(s, pf, ts);
-    bool redo = false;
-#pragma unroll
-    for (int qb = 0; qb < NQB; ++qb) redo = redo || !(ts[qb] <= kMaxTileSum);
-    if (__any(redo)) {
-      floatx16 init[NQB];
-#pragma unroll
-      for (int qb = 0; qb < NQB; ++qb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) init[qb][r] = 0.f;
-      qk(s, init);
+      for (int qb = 0; qb < NQB; ++qb) bad = bad || !(ts[qb] <= kMaxBlockSum);
+      return !__any(bad);
+    };
+    // the redo of key blocks kb0..kb1 from raw scores already in s: m raised
+    // to their max where that exceeds it by more than kRaise (O and l
+    // rescaled), then offset scores and exponentials again
+    auto redo = [&](int kb0, int kb1, floatx16 (&s)[2][NQB], Frag (&pf)[2][NCH][NQB], float (&ts)[NQB]) {
 #pragma unroll
       for (int qb = 0; qb < NQB; ++qb) {
-        float x = s[0][qb][0];
+        float x = s[kb0][qb][0];
 #pragma unroll
-        for (int r = 1; r < 16; ++r) x = fmaxf(x, s[0][qb][r]);
+        for (int kb = kb0; kb <= kb1; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) x = fmaxf(x, s[1][qb][r]);
+          for (int r = 0; r < 16; ++r) x = fmaxf(x, s[kb][qb][r]);
         const float mx = half_swap_max(x);
         if (mx > m[qb] + kRaise) {
           const float mn = M::exact(mx);
           const float alpha = __builtin_amdgcn_exp2f(m[qb] - mn);  // 0 while m = -inf
           m[qb] = mn;
-          nm[qb] = M::seed(-mn, hi);
+          nm[qb] = M::seed_b(-mn, hi);
           o[0][qb] *= alpha;
           o[1][qb] *= alpha;
           l[qb] *= alpha;
@@ -782,30 +759,109 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
         // a column with no valid key so far keeps m = -inf: its P is 0
         const float off = m[qb] == -INFINITY ? 0.f : m[qb];
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int kb = kb0; kb <= kb1; ++kb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) s[kb][qb][r] -= off;
       }
-      expsum(s, pf, ts);
-    }
-#pragma unroll
-    for (int qb = 0; qb < NQB; ++qb) l[qb] += ts[qb];
-
-    // O^T += V^T P^T
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+      exp_block(kb0, s, pf, ts);
+    };
+    // O^T += V^T P^T over key block kb
+    auto pv_block = [&](int kb, const Frag (&pf)[2][NCH][NQB]) {
+      Frag vf[NCH][2];
 #pragma unroll
       for (int ch = 0; ch < NCH; ++ch)
 #pragma unroll
-        for (int db = 0; db < 2; ++db) {
-          Frag vf = read_v(cv, L::VP, db * 32 + l32, kb, ch, hi);
+        for (int db = 0; db < 2; ++db) vf[ch][db] = read_v(cv, L::VP, db * 32 + l32, kb, ch, hi);
 #pragma unroll
-          for (int qb = 0; qb < NQB; ++qb) o[db][qb] = M::mma(vf, pf[kb][ch][qb], o[db][qb]);
+      for (int ch = 0; ch < NCH; ++ch)
+#pragma unroll
+        for (int db = 0; db < 2; ++db)
+#pragma unroll
+          for (int qb = 0; qb < NQB; ++qb) o[db][qb] = M::mma(vf[ch][db], pf[kb][ch][qb], o[db][qb]);
+    };
+
+    floatx16 s[2][NQB];
+    Frag pf[2][NCH][NQB];
+    float ts[NQB];
+    if constexpr (sizeof(T) == 2 && !QLDS) {
+      // Two 32-key blocks in flight: block 0's exponentials run beside block
+      // 1's QK MFMAs, block 1's beside block 0's PV MFMAs.  Each block's sums
+      // are checked before its PV; block 0's redo covers both blocks (block
+      // 1's scores carry the old offset), block 1's only itself.
+      Frag kf[2][NDC];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int dc = 0; dc < NDC; ++dc) kf[kb][dc] = read_k(ck, L::KP, kb * 32 + l32, dc, hi);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        seed(kb, false, s[kb]);
+#pragma unroll
+        for (int dc = 0; dc < NDC; ++dc)
+#pragma unroll
+          for (int qb = 0; qb < NQB; ++qb) s[kb][qb] = M::mma(kf[kb][dc], qf[qb][dc], s[kb][qb]);
+      }
+      exp_block(0, s, pf, ts);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * NDC, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, NQB * (NDC + 2), 0);
+#pragma unroll
+      for (int i = 0; i < NDC * NQB; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+      }
+      if (!sums_ok(ts)) {
+        qk_tile(s, true);
+        redo(0, 1, s, pf, ts);
+      }
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) l[qb] += ts[qb];
+
+      pv_block(0, pf);
+      exp_block(1, s, pf, ts);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * NCH, 0);
+#pragma unroll
+      for (int i = 0; i < 2 * NCH * NQB; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+      }
+      if (!sums_ok(ts)) {
+        seed(1, true, s[1]);
+#pragma unroll
+        for (int dc = 0; dc < NDC; ++dc) {
+          const Frag kf1 = read_k(ck, L::KP, 32 + l32, dc, hi);
+#pragma unroll
+          for (int qb = 0; qb < NQB; ++qb) s[1][qb] = M::mma(kf1, qf[qb][dc], s[1][qb]);
         }
+        redo(1, 1, s, pf, ts);
+      }
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) l[qb] += ts[qb];
+      pv_block(1, pf);
+    } else {
+      // fp32, and bf16 with queries in LDS: the whole tile at once
+      qk_tile(s, false);
+      float t1s[NQB];
+      exp_block(0, s, pf, ts);
+      exp_block(1, s, pf, t1s);
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) ts[qb] += t1s[qb];
+      if (!sums_ok(ts)) {
+        qk_tile(s, true);
+        redo(0, 1, s, pf, ts);
+        exp_block(1, s, pf, t1s);
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb) ts[qb] += t1s[qb];
+      }
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) l[qb] += ts[qb];
+      pv_block(0, pf);
+      pv_block(1, pf);
+    }
 
     // the other buffer was last read in the previous tile, before its barrier
     if (more) ld.store(lt[buf ^ 1], tid);
-    cur_lens = ld.dlens;
+    cur_lens[0] = ld.dlens[0];
+    cur_lens[1] = ld.dlens[1];
     __syncthreads();
   }
 
