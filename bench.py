@@ -9,8 +9,10 @@ region.  Each frame is one gca_step call: one launch for the append, eviction,
 query rotation and gather list, then the attention and the split merge.  The
 attention kernel's duration comes from HIP events that the library records
 around each of its launches on the stream it launches on; the roofline
-uses the algorithmic FLOPs 4*T*H*D*n_ctx per frame.  The other kernels'
-durations come from a rocprofv3 kernel trace of the same command.
+uses the algorithmic FLOPs 4*T*H*D*n_ctx per frame.  After the timed region
+the append and compaction launches (the individual calls) are timed in
+back-to-back batches for their HBM roofline (`append_compact`).  The other
+kernels' durations come from a rocprofv3 kernel trace of the same command.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 """
@@ -140,10 +142,81 @@ def run_gpu(w, steps, warmup):
     t1 = time.perf_counter()
     kern = {"attn": cache.profile_read("attn")}
     cache.profile_enable(0)
-    # a replay of one stream with the output checked for sanity
     assert torch.isfinite(out).all()
+
+    # Append and compaction as their own launches (the individual calls), timed
+    # in back-to-back batches with HIP events on the launch stream around each
+    # batch: per-launch time = kernel plus the dispatch gap to the next one.  A
+    # spin kernel ahead of the batch holds the stream until every launch is
+    # queued, so host-side call overhead is not timed.
+    def batch(fn):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda._sleep(20_000_000)
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1)
+
+    def appends():  # TEMP appends of frames 0..n-1 on an empty cache, each rolled back (host only)
+        for f in range(w.n_frames):
+            if cache.append_frame(f, K[f % n_stage], V[f % n_stage], temp=True, stream=stream) != 0 or \
+                    cache.rollback_last_frame(f, stream) != 0:
+                raise RuntimeError("append batch failed")
+
+    for timed in (False, True):
+        if cache.reset(stream) != 0:
+            raise RuntimeError("reset failed")
+        torch.cuda.synchronize()
+        if timed:
+            append_ms = batch(appends) / w.n_frames
+        else:
+            appends()
+    fill = w.A + w.W  # keyframes that fit before the first eviction
+    kf = [f for f in range(w.n_frames) if w.is_keyframe(f)]
+    n_evict = 0
+    if w.C > 0 and len(kf) > fill:
+        if cache.reset(stream) != 0:
+            raise RuntimeError("reset failed")
+        for f in kf[:fill]:
+            if cache.append_frame(f, K[f % n_stage], V[f % n_stage], stream=stream) != 0:
+                raise RuntimeError("fill failed")
+
+        def pairs():
+            for f in kf[fill:]:
+                if cache.append_frame(f, K[f % n_stage], V[f % n_stage], stream=stream) != 0 or \
+                        cache.evict_compact(stream) != 0:
+                    raise RuntimeError("eviction batch failed")
+        torch.cuda.synchronize()
+        n_evict = len(kf) - fill
+        pair_ms = batch(pairs) / n_evict
+    kern["append"] = (append_ms, 1)
+    kern["evict"] = (pair_ms - append_ms, 1) if n_evict else (0.0, 0)
     cache.close()
     return dict(seconds=t1 - t0, kern=kern, flop_stream=flop_stream, n_ctx=n_ctx)
+
+
+def append_compact_line(w, kern):
+    """HBM roofline of the append and compaction launches (algorithmic bytes per launch)."""
+    esize = 2 if w.dtype == "bf16" else 4
+    ppf = -(-w.T // w.P)
+    row = w.H * w.D * esize
+    # append: read the frame's K and V, write both into its pages (zero tail included)
+    append_b = 2 * w.T * row + 2 * ppf * w.P * row
+    # compaction: read C tokens' K and V from the evicted frame's pages, write them to trajectory pages
+    evict_b = 4 * w.C * row
+    out = {}
+    for name, b in (("append", append_b), ("compact", evict_b)):
+        ms, n = kern["append" if name == "append" else "evict"]
+        if n == 0 or ms <= 0:
+            continue
+        us = ms * 1e3 / n
+        gbs = b / (us * 1e-6) / 1e9
+        out[name] = {"us_per_launch": round(us, 3), "bytes": b, "achieved": round(gbs, 1),
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4)}
+    out["timing"] = ("back-to-back batches (one TEMP append per frame; append+evict pairs minus appends), "
+                     "HIP events on the launch stream around each batch")
+    return out
 
 
 def run_cpu_baseline(w, rows_per_frame):
@@ -231,6 +304,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(achieved / peak, 4),
                      "traffic": (traffic if traffic is None else round(traffic))},
+        "append_compact": append_compact_line(w, r["kern"]),
         "attn_ms_avg": round(attn_ms / max(attn_n, 1), 5),
         "mean_n_ctx": round(sum(r["n_ctx"]) / len(r["n_ctx"]), 1),
         "attn_flop_per_launch": flop_per_launch,
