@@ -9,10 +9,12 @@ region.  Each frame is one gca_step call: one launch for the append, eviction,
 query rotation and gather list, then the attention and the split merge.  The
 attention kernel's duration comes from HIP events that the library records
 around each of its launches on the stream it launches on; the roofline
-uses the algorithmic FLOPs 4*T*H*D*n_ctx per frame.  After the timed region
-the append and compaction launches (the individual calls) are timed in
-back-to-back batches for their HBM roofline (`append_compact`).  The other
-kernels' durations come from a rocprofv3 kernel trace of the same command.
+uses the algorithmic FLOPs 4*T*H*D*n_ctx per frame.  Events at the start of
+the last 10 % of each stream's frames give the steady-state rate.  After the
+timed region the append and compaction launches (the individual calls) are timed in
+back-to-back batches for their HBM roofline (`append_compact`).  MFMA busy and
+HBM traffic come from the committed rocprofv3 counter summary of the same
+kernel source; the other kernels' durations from a rocprofv3 kernel trace.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 """
@@ -66,16 +68,14 @@ def kernel_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def traffic_from_profiles(kh: str):
-    """HBM bytes per attention launch from the committed counter summary, if current."""
+def counters_from_profiles(kh: str) -> dict:
+    """The committed counter summary of the attention kernel, if it is of this source."""
     p = os.path.join(ROOT, "profiles", "attn_traffic.json")
     try:
         d = json.load(open(p))
     except (OSError, ValueError):
-        return None
-    if d.get("kernel_hash") != kh:
-        return None
-    return d.get("bytes_per_launch")
+        return {}
+    return d if d.get("kernel_hash") == kh else {}
 
 
 def run_gpu(w, steps, warmup):
@@ -103,15 +103,27 @@ def run_gpu(w, steps, warmup):
     lse = torch.empty((w.T, w.H), dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream()
 
-    def one_stream():
+    # the last 10 % of each stream (the longest contexts): events on the stream
+    f_tail = w.n_frames - max(1, w.n_frames // 10)
+    tail_ev = []
+
+    def one_stream(mark_tail=False):
         if cache.reset(stream) != 0:
             raise RuntimeError("reset failed")
         for f in range(w.n_frames):
+            if mark_tail and f == f_tail:
+                e = torch.cuda.Event(enable_timing=True)
+                e.record(stream)
+                tail_ev.append(e)
             i = f % n_stage
             # append (+ evict) + attend (+ rollback): one update launch, then attention
             rc = cache.step(f, K[i], V[i], Q[i], out, lse, keyframe=w.is_keyframe(f), stream=stream)
             if rc != 0:
                 raise RuntimeError(f"frame {f}: {gca.status_string(rc)}")
+        if mark_tail:
+            e = torch.cuda.Event(enable_timing=True)
+            e.record(stream)
+            tail_ev.append(e)
 
     # context length per frame (data independent) from the host planner
     plan = gca.Plan(gca.Config.from_workload(w))
@@ -137,12 +149,15 @@ def run_gpu(w, steps, warmup):
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(steps):
-        one_stream()
+        one_stream(mark_tail=True)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     kern = {"attn": cache.profile_read("attn")}
     cache.profile_enable(0)
     assert torch.isfinite(out).all()
+    tail_ms = sum(tail_ev[2 * i].elapsed_time(tail_ev[2 * i + 1]) for i in range(steps))
+    tail_fps = steps * (w.n_frames - f_tail) / (tail_ms * 1e-3)
+
 
     # Append and compaction as their own launches (the individual calls), timed
     # in back-to-back batches with HIP events on the launch stream around each
@@ -193,7 +208,11 @@ def run_gpu(w, steps, warmup):
     kern["append"] = (append_ms, 1)
     kern["evict"] = (pair_ms - append_ms, 1) if n_evict else (0.0, 0)
     cache.close()
-    return dict(seconds=t1 - t0, kern=kern, flop_stream=flop_stream, n_ctx=n_ctx)
+    props = torch.cuda.get_device_properties(0)
+    device = {"name": props.name, "gcn_arch": getattr(props, "gcnArchName", None),
+              "compute_units": props.multi_processor_count, "hip": torch.version.hip}
+    return dict(seconds=t1 - t0, kern=kern, flop_stream=flop_stream, n_ctx=n_ctx, tail_fps=tail_fps,
+                tail_frames=(f_tail, w.n_frames), device=device)
 
 
 def append_compact_line(w, kern):
@@ -257,7 +276,15 @@ def run_cpu_baseline(w, rows_per_frame):
         per_row = max(0.0, (e - m) - one) / max(1, len(rows) - 1)
         t_attn += one + per_row * w.T    # all T query rows
     est = t_book + t_attn
-    return dict(value=n_frames / est, unit="frames/s/layer", cores=threads, kind="oracle",
+    model = None
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                model = ln.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return dict(value=n_frames / est, unit="frames/s/layer", cores=threads, kind="oracle", cpu_model=model,
                 sample=(f"first {n_frames} frames of {w.name}: every append/evict plus attention "
                         f"for {len(rows)} of {w.T} query rows per frame (and 1 row, to separate "
                         f"the fixed cost); full-row time scaled linearly in rows; "
@@ -283,7 +310,9 @@ def main():
     achieved = flop_per_launch / avg_attn_s / 1e12
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_MFMA_TFLOPS
     kh = kernel_hash()
-    traffic = traffic_from_profiles(kh)
+    ctr = counters_from_profiles(kh)
+    traffic = ctr.get("bytes_per_launch")
+
     line = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -304,11 +333,15 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(achieved / peak, 4),
                      "traffic": (traffic if traffic is None else round(traffic))},
+        "steady_state": {"frames": list(r["tail_frames"]), "value": round(r["tail_fps"], 2),
+                         "unit": "frames/s/layer"},
+        "mfma_busy": ctr.get("mfma_busy"),
         "append_compact": append_compact_line(w, r["kern"]),
         "attn_ms_avg": round(attn_ms / max(attn_n, 1), 5),
         "mean_n_ctx": round(sum(r["n_ctx"]) / len(r["n_ctx"]), 1),
         "attn_flop_per_launch": flop_per_launch,
         "kernel_hash": kh,
+        "device": r["device"],
     }
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
