@@ -107,6 +107,12 @@ struct MergeArgs {
   int out_bf16;
 };
 
+// bf16 V pools hold each 16-slot group of a page row in P-operand order:
+// slots 0-3, 8-11, 4-7, 12-15 (storage position s holds slot vslot(s); the
+// map swaps bits 2 and 3 and is its own inverse), so that a 16-byte chunk of
+// a V^T row is one MFMA operand.  fp32 pools keep slot order.
+__host__ __device__ inline int vslot(int s) { return (s & ~12) | ((s & 4) << 1) | ((s & 8) >> 1); }
+
 struct RopeArgs {
   const void* x;
   void* y;

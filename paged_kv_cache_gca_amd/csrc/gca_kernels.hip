@@ -151,7 +151,10 @@ __device__ inline void append_block(const AppendArgs& a, int i, int h) {
     int d = c / cpk, kc = c - d * cpk;
     Vec16<T> o;
 #pragma unroll
-    for (int e = 0; e < EPC; ++e) o.e[e] = lds[(kc * EPC + e) * LP + d];
+    for (int e = 0; e < EPC; ++e) {
+      const int slot = sizeof(T) == 2 ? vslot(kc * EPC + e) : kc * EPC + e;
+      o.e[e] = lds[slot * LP + d];
+    }
     *(uint4*)(vp + (size_t)d * a.P + kc * EPC) = o.u;
   }
 }
@@ -195,8 +198,9 @@ __device__ inline void evict_block(const EvictArgs& a, int b) {
                                   : a.ring[(a.ring_head + (pi - a.n_traj_pages)) % a.N];
     kp[(((size_t)dst * a.H + h) * a.P + ds) * kHeadDim + d] =
         kp[(((size_t)src * a.H + h) * a.P + ss) * kHeadDim + d];
-    vp[(((size_t)dst * a.H + h) * kHeadDim + d) * a.P + ds] =
-        vp[(((size_t)src * a.H + h) * kHeadDim + d) * a.P + ss];
+    const int vd = sizeof(T) == 2 ? vslot(ds) : ds, vs = sizeof(T) == 2 ? vslot(ss) : ss;
+    vp[(((size_t)dst * a.H + h) * kHeadDim + d) * a.P + vd] =
+        vp[(((size_t)src * a.H + h) * kHeadDim + d) * a.P + vs];
   }
   if (grp != 0) return;
   // slots of the last written trajectory page past the new end stay zero (a
@@ -211,7 +215,8 @@ __device__ inline void evict_block(const EvictArgs& a, int b) {
     for (int idx = tid; idx < n; idx += 256) {
       int jj = idx / kHeadDim, dd = idx - jj * kHeadDim;
       kp[(((size_t)dst * a.H + h) * a.P + fill + jj) * kHeadDim + dd] = from_f<T>(0.f);
-      vp[(((size_t)dst * a.H + h) * kHeadDim + dd) * a.P + fill + jj] = from_f<T>(0.f);
+      const int vz = sizeof(T) == 2 ? vslot(fill + jj) : fill + jj;
+      vp[(((size_t)dst * a.H + h) * kHeadDim + dd) * a.P + vz] = from_f<T>(0.f);
     }
   }
   if (h == 0) {
@@ -381,9 +386,16 @@ struct Mfma<float> {
   __device__ static inline float exact(float x) { return x; }
 };
 
+// bf16 tiles in LDS: 64 rows of 128 bytes (K: key rows of 64 dims; V^T: dim
+// rows of 64 keys), no padding.  The 16-byte chunk c of row r sits at chunk
+// position c ^ (r & 7) of its row, so the eight rows that one read
+// instruction's lane groups touch hit eight different bank groups.
+__device__ inline int swz(int row, int c) { return row * 128 + ((c ^ (row & 7)) << 4); }
+
 // K operand: key row `row`, dims [dc*2*KPL + hi*KPL, +KPL).
 __device__ inline bf16x8 read_k(const bf16* lk, int pitch, int row, int dc, int hi) {
-  return *(const bf16x8*)(lk + row * pitch + dc * 16 + hi * 8);
+  (void)pitch;
+  return *(const bf16x8*)((const char*)lk + swz(row, dc * 2 + hi));
 }
 __device__ inline float read_k(const float* lk, int pitch, int row, int dc, int hi) {
   return lk[row * pitch + dc * 2 + hi];
@@ -395,7 +407,8 @@ __device__ inline float read_k(const float* lk, int pitch, int row, int dc, int 
 // V^T tile holds each 16-key group in that order (keys 0-3, 8-11, 4-7,
 // 12-15), so the operand is one 16-byte read, laid out like the K reads.
 __device__ inline bf16x8 read_v(const bf16* lv, int pitch, int d, int kb, int ch, int hi) {
-  return *(const bf16x8*)(lv + d * pitch + kb * 32 + ch * 16 + hi * 8);
+  (void)pitch;
+  return *(const bf16x8*)((const char*)lv + swz(d, kb * 4 + ch * 2 + hi));
 }
 __device__ inline float read_v(const float* lv, int pitch, int d, int kb, int ch, int hi) {
   return lv[d * pitch + kb * 32 + (ch >> 2) * 8 + hi * 4 + (ch & 3)];
@@ -448,8 +461,11 @@ struct TileLoader {
   static constexpr int CPRK = kHeadDim / EPC;          // chunks per K row
   static constexpr int CPRV = kKeysPerTile / EPC;      // chunks per V^T row
   static constexpr int NC = kKeysPerTile * CPRK / 256; // chunks per thread (K and V alike)
-  static constexpr int KP = kHeadDim + EPC;            // LDS pitches (one 16-byte pad)
-  static constexpr int VP = kKeysPerTile + EPC;
+  // LDS layout: bf16 as the swizzled 128-byte rows the operand reads expect
+  // (swz); fp32 rows padded by 16 bytes
+  static constexpr bool SWZ = sizeof(T) == 2;
+  static constexpr int KP = SWZ ? kHeadDim : kHeadDim + EPC;
+  static constexpr int VP = SWZ ? kKeysPerTile : kKeysPerTile + EPC;
   static constexpr int TILE_ELEMS = kKeysPerTile * KP + kHeadDim * VP;
 
   // chunk i of thread t: K row r = c / CPRK, part c % CPRK; V^T row d = c / CPRV,
@@ -514,21 +530,109 @@ struct TileLoader {
   __device__ void store(T* tileb, int tid) {
 #pragma unroll
     for (int i = 0; i < NC; ++i) {
-      *(u32x4*)(tileb + k_row(tid, i) * KP + k_part(tid) * EPC) = kr[i];
-      T* vrow = tileb + kKeysPerTile * KP + v_row(tid, i) * VP;
-      if constexpr (sizeof(T) == 2) {
-        // keys 8j..8j+7: the first four go to 16*(j/2) + 4*(j%2), the
-        // other four 8 elements further (the operand order of read_v)
-        const int j = v_key0(tid) / 8;
-        T* dst = vrow + (j >> 1) * 16 + (j & 1) * 4;
-        *(u32x2*)dst = vr[i].xy;
-        *(u32x2*)(dst + 8) = vr[i].zw;
+      if constexpr (SWZ) {
+        char* kt = (char*)tileb;
+        *(u32x4*)(kt + swz(k_row(tid, i), k_part(tid))) = kr[i];
+        *(u32x4*)(kt + kKeysPerTile * KP * 2 + swz(v_row(tid, i), v_key0(tid) / EPC)) = vr[i];
       } else {
-        *(u32x4*)(vrow + v_key0(tid)) = vr[i];
+        *(u32x4*)(tileb + k_row(tid, i) * KP + k_part(tid) * EPC) = kr[i];
+        *(u32x4*)(tileb + kKeysPerTile * KP + v_row(tid, i) * VP + v_key0(tid)) = vr[i];
       }
     }
   }
 };
+
+__device__ inline int pick(i32x4 v, int j) { return j == 0 ? v.x : j == 1 ? v.y : j == 2 ? v.z : v.w; }
+
+// bf16 tiles go straight from HBM/L2 into LDS (global_load_lds: each lane's
+// 16 bytes land at the instruction's LDS base + lane * 16), three buffers
+// deep, so a tile's loads have two tiles of math to land and no registers
+// hold tile data.  Each lane loads the 16-byte piece that belongs at its
+// (swizzled) LDS position: 2 instructions per wave for K and 2 for V^T, whose
+// pool rows are already in operand order (vslot).  Page ids and entry
+// lengths are loaded one tile before the tile's data, with plain per-lane
+// vector loads.
+template <int P>
+struct DmaLoader {
+  static constexpr int EPT = kKeysPerTile / P;
+  static constexpr int KBYTES = kKeysPerTile * kHeadDim * 2;  // 8 KB, then V^T 8 KB
+  static constexpr int BUF_BYTES = 2 * KBYTES;
+  static constexpr int NFETCH = 2;  // vector loads per fetch: the tile's page ids, its lengths
+  static constexpr int NISSUE = 4;  // DMA loads per wave and tile
+  // the EPT page ids and lengths of a tile, as loaded (every lane loads the
+  // same 4 to 16 bytes); each lane picks its pieces' entries when it issues
+  struct Ids {
+    i32x4 pg, ln;
+  };
+  uint32_t koff[2], voff[2];  // piece offsets inside a (page, head) block (bytes)
+  int kent[2], vent[2];       // their gather entries within a tile
+  uint32_t page_bytes, head_off;
+
+  __device__ void init(int h, int H, int tid) {
+    const int w = tid >> 6, lane = tid & 63;
+    page_bytes = (uint32_t)(H * P * kHeadDim * 2);
+    head_off = (uint32_t)(h * P * kHeadDim * 2);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int pos = (w * 2 + j) * 64 + lane;        // 16-byte position in the K tile
+      const int r = pos >> 3, c = (pos & 7) ^ (r & 7);  // key row, logical chunk
+      kent[j] = r / P;
+      koff[j] = (uint32_t)(((r % P) * kHeadDim + c * 8) * 2);
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int pos = (w * 2 + j) * 64 + lane;        // 16-byte position in the V^T tile
+      const int d = pos >> 3, c = (pos & 7) ^ (d & 7);  // dim row, chunk (8 stored slots)
+      vent[j] = (8 * c) / P;
+      voff[j] = (uint32_t)((d * P + (8 * c) % P) * 2);
+    }
+  }
+  template <int N>
+  __device__ static i32x4 load_n(const int32_t* p) {
+    i32x4 v = {0, 0, 0, 0};
+    if constexpr (N == 4) {
+      v = *(const i32x4*)p;
+    } else if constexpr (N == 2) {
+      const i32x2 u = *(const i32x2*)p;
+      v.x = u.x;
+      v.y = u.y;
+    } else {
+      v.x = *p;
+    }
+    return v;
+  }
+  __device__ void fetch(const AttnArgs& a, int tile, Ids& x) const {
+    x.pg = load_n<EPT>(a.sel_page + tile * EPT);
+    x.ln = load_n<EPT>(a.sel_len + tile * EPT);
+  }
+  // entry lengths of keys l32 and 32 + l32
+  __device__ static void lens_of(const Ids& x, int l32, int (&out)[2]) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) out[kb] = pick(x.ln, (kb * 32 + l32) / P);
+  }
+  __device__ void issue(const char* kpool, const char* vpool, const Ids& x, char* buf, int w) const {
+    typedef __attribute__((address_space(3))) void lds_t;
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      __builtin_amdgcn_global_load_lds(kpool + (uint64_t)(uint32_t)pick(x.pg, kent[j]) * page_bytes + head_off +
+                                           koff[j],
+                                       (lds_t*)(buf + (w * 2 + j) * 1024), 16, 0, 0);
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      __builtin_amdgcn_global_load_lds(vpool + (uint64_t)(uint32_t)pick(x.pg, vent[j]) * page_bytes + head_off +
+                                           voff[j],
+                                       (lds_t*)(buf + KBYTES + (w * 2 + j) * 1024), 16, 0, 0);
+  }
+};
+
+// s_waitcnt on the vector-memory count only (vmcnt <= N, N < 16): bits 3:0
+// vmcnt, 6:4 expcnt (7: no wait), 11:8 lgkmcnt (15: no wait), 15:14 the high
+// vmcnt bits (0 here)
+template <int N>
+__device__ inline void wait_vmem() {
+  static_assert(N >= 0 && N < 16, "vmcnt immediate");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+}
 
 // Row sums of P from the same rounded values the P.V product uses (this
 // lane's keys only; the lane pair l, l ^ 32 covers the whole tile).
@@ -558,20 +662,20 @@ template <typename T, int P>
 __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
   using M = Mfma<T>;
   using Frag = typename M::Frag;
-  using L = TileLoader<T, P>;
+  using L = TileLoader<T, P>;   // fp32: through registers, two buffers
+  using DL = DmaLoader<P>;      // bf16: straight into LDS, three buffers
+  // bf16 tiles: straight into LDS at P = 64, through registers at P = 16/32
+  // (measured faster each way)
+  constexpr bool DMA = sizeof(T) == 2 && P == 64;
   constexpr int NQB = M::NQB;
   constexpr int KPL = M::KPL;
   constexpr int NDC = kHeadDim / (2 * KPL);  // MFMAs along the head dim
   constexpr int NCH = 16 / KPL;              // P^T operands per 32-key block
-  constexpr int EPT = L::EPT;
   constexpr int QPW = NQB * 32;              // queries per wave
-  __shared__ __attribute__((aligned(16))) T lt[2][L::TILE_ELEMS];  // double-buffered tiles
-  // Query fragments stay in registers (B operands) except for bf16 with
-  // P = 64, where they wait in LDS in operand order [qb][dc][lane]
-  // (conflict-free 16-byte reads) and each tile runs as one block (measured
-  // faster there; at P = 16 and 32 registers and the two-block pipeline are).
-  constexpr bool QLDS = sizeof(T) == 2 && P == 64;
-  __shared__ __attribute__((aligned(16))) Frag lq[QLDS ? kWaves * NQB * NDC * 64 : 1];
+  constexpr int NBUF = DMA ? 3 : 2;
+  constexpr int BUF_ELEMS = DMA ? DL::BUF_BYTES / (int)sizeof(T) : L::TILE_ELEMS;
+  constexpr int VOFF = DMA ? kKeysPerTile * kHeadDim : kKeysPerTile * L::KP;  // V^T within a buffer
+  __shared__ __attribute__((aligned(16))) T lt[NBUF][BUF_ELEMS];
 
   // workgroup -> (head, split, q tile).  Dispatch is round-robin over the
   // XCDs, each with its own L2.  With H a multiple of 8, all workgroups of a
@@ -621,28 +725,9 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
   const T* kpool = (const T*)a.kpool;
   const T* vpool = (const T*)a.vpool;
 
-  L ld;
-  ld.init(kpool, vpool, h, a.H, tid);
-  if (t0 < t1) {
-    ld.fetch_pages(a, t0, tid);
-    ld.fetch_data(tid);
-    ld.fetch_pages(a, t0 + 1, tid);
-  }
-  Frag qf[QLDS ? 1 : NQB][QLDS ? 1 : NDC];
-  Frag* mq = lq + wave * (NQB * NDC * 64);
-  if constexpr (QLDS) {
-    Frag qtmp[NQB][NDC];
-    load_q(a, qbase, h, l32, hi, qtmp);
-#pragma unroll
-    for (int qb = 0; qb < NQB; ++qb)
-#pragma unroll
-      for (int dc = 0; dc < NDC; ++dc) mq[(qb * NDC + dc) * 64 + lane] = qtmp[qb][dc];
-  } else {
-    load_q(a, qbase, h, l32, hi, qf);
-  }
-  if (t0 < t1) ld.store(lt[t0 & 1], tid);
-  int cur_lens[2] = {ld.dlens[0], ld.dlens[1]};  // entry lengths of the tile in LDS
-  __syncthreads();
+  // the wave's query fragments stay in registers (B operands)
+  Frag qf[NQB][NDC];
+  load_q(a, qbase, h, l32, hi, qf);
 
   floatx16 o[2][NQB];
 #pragma unroll
@@ -672,16 +757,9 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
   constexpr float kMaxBlockSum = 65536.f;
   constexpr float kRaise = 8.f;
 
-  for (int tile = t0; tile < t1; ++tile) {
-    const int buf = tile & 1;
-    const bool more = tile + 1 < t1;
-    if (more) {
-      ld.fetch_data(tid);                         // tile + 1, lands during this tile's math
-      ld.fetch_pages(a, tile + 2, tid);           // page ids two tiles ahead
-    }
-    const T* ck = lt[buf];
-    const T* cv = lt[buf] + kKeysPerTile * L::KP;
-
+  // one 64-key tile from LDS: K at ck, V^T at cv, entry lengths of keys l32
+  // and 32 + l32 in cur_lens
+  auto compute_tile = [&](const T* ck, const T* cv, const int (&cur_lens)[2]) {
     // seed A operands: key kb*32 + l32 is masked when past its gather
     // entry's valid length (partial pages)
     typename M::Seed sa[2];
@@ -700,20 +778,13 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
       seed(0, raw, s[0]);
       seed(1, raw, s[1]);
 #pragma unroll
-      for (int dc = 0; dc < NDC; ++dc) {
-        Frag qv[NQB];
-#pragma unroll
-        for (int qb = 0; qb < NQB; ++qb) {
-          if constexpr (QLDS) qv[qb] = mq[(qb * NDC + dc) * 64 + lane];
-          else qv[qb] = qf[qb][dc];
-        }
+      for (int dc = 0; dc < NDC; ++dc)
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
           Frag kf = read_k(ck, L::KP, kb * 32 + l32, dc, hi);
 #pragma unroll
-          for (int qb = 0; qb < NQB; ++qb) s[kb][qb] = M::mma(kf, qv[qb], s[kb][qb]);
+          for (int qb = 0; qb < NQB; ++qb) s[kb][qb] = M::mma(kf, qf[qb][dc], s[kb][qb]);
         }
-      }
     };
     // exponentials, packing and this lane's sums of key block kb
     auto exp_block = [&](int kb, floatx16 (&s)[2][NQB], Frag (&pf)[2][NCH][NQB], float (&ts)[NQB]) {
@@ -783,7 +854,7 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
     floatx16 s[2][NQB];
     Frag pf[2][NCH][NQB];
     float ts[NQB];
-    if constexpr (sizeof(T) == 2 && !QLDS) {
+    if constexpr (sizeof(T) == 2) {
       // Two 32-key blocks in flight: block 0's exponentials run beside block
       // 1's QK MFMAs, block 1's beside block 0's PV MFMAs.  Each block's sums
       // are checked before its PV; block 0's redo covers both blocks (block
@@ -838,7 +909,7 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
       for (int qb = 0; qb < NQB; ++qb) l[qb] += ts[qb];
       pv_block(1, pf);
     } else {
-      // fp32, and bf16 with queries in LDS: the whole tile at once
+      // fp32: the whole tile at once
       qk_tile(s, false);
       float t1s[NQB];
       exp_block(0, s, pf, ts);
@@ -858,11 +929,100 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
       pv_block(1, pf);
     }
 
-    // the other buffer was last read in the previous tile, before its barrier
-    if (more) ld.store(lt[buf ^ 1], tid);
-    cur_lens[0] = ld.dlens[0];
-    cur_lens[1] = ld.dlens[1];
+  };
+
+  const int n = max(t1 - t0, 0);
+  if constexpr (DMA) {
+   if (n > 0) {
+    // Every iteration fetches and issues unconditionally: a split that has
+    // tiles reads at most three tiles past its end, which the gather list's
+    // padding covers (pad entries name the zero page).  So
+    // each iteration adds the same vector-memory operations, in the same
+    // order: the ids of tile i + 3 (NFETCH), then tile i + 2's data (NISSUE).
+    // Waiting until at most NISSUE are in flight at the end of iteration i
+    // leaves only tile i + 2's data outstanding: tile i + 1 has landed and
+    // the ids of tile i + 3 are in registers (the compiler counts the same
+    // way and adds no wait before they are used).
+    DL ld;
+    ld.init(h, a.H, tid);
+    typename DL::Ids ide, ido;  // ids of the tiles at even / odd distance from t0
+    int lc[2], l1[2], l2[2];    // lengths: this tile, next, next but one
+    const char* kp = (const char*)a.kpool;
+    const char* vp = (const char*)a.vpool;
+    char* lbase = (char*)&lt[0][0];
+    constexpr int BB = DL::BUF_BYTES;
+    auto ready = [](typename DL::Ids& x) {
+      asm volatile("" : "+v"(x.pg), "+v"(x.ln));
+    };
+    ld.fetch(a, t0, ide);
+    ld.fetch(a, t0 + 1, ido);
+    __builtin_amdgcn_s_waitcnt(0);  // the queries and the first ids
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb)
+#pragma unroll
+      for (int dc = 0; dc < NDC; ++dc) asm volatile("" : "+v"(qf[qb][dc]));
+    ready(ide);
+    ready(ido);
+    asm volatile("" ::: "memory");
+    ld.issue(kp, vp, ide, lbase, wave);
+    DL::lens_of(ide, l32, lc);
+    ld.fetch(a, t0 + 2, ide);
+    ld.issue(kp, vp, ido, lbase + BB, wave);
+    DL::lens_of(ido, l32, l1);
+    asm volatile("" ::: "memory");
+    wait_vmem<DL::NISSUE>();  // tile t0 and the ids of tile t0 + 2 have landed
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    auto step = [&](int i, typename DL::Ids& fx, const typename DL::Ids& iy) {
+      ld.fetch(a, t0 + i + 3, fx);
+      ld.issue(kp, vp, iy, lbase + ((i + 2) % 3) * BB, wave);
+      DL::lens_of(iy, l32, l2);
+      asm volatile("" ::: "memory");  // the loads above stay ahead of the count below
+      const T* ck = lt[i % 3];
+      compute_tile(ck, ck + VOFF, lc);
+      asm volatile("" ::: "memory");
+      wait_vmem<DL::NISSUE>();
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();  // buffer i % 3 is free, tile i + 1 visible to all waves
+      asm volatile("" ::: "memory");
+      lc[0] = l1[0];
+      lc[1] = l1[1];
+      l1[0] = l2[0];
+      l1[1] = l2[1];
+    };
+    for (int i = 0; i < n; i += 2) {
+      step(i, ido, ide);
+      if (i + 1 < n) step(i + 1, ide, ido);
+    }
+    // the loads issued past the last tile land before the workgroup's LDS is released
+    wait_vmem<0>();
+   }
+  } else {
+    L ld;
+    ld.init(kpool, vpool, h, a.H, tid);
+    if (n > 0) {
+      ld.fetch_pages(a, t0, tid);
+      ld.fetch_data(tid);
+      ld.fetch_pages(a, t0 + 1, tid);
+      ld.store(lt[t0 & 1], tid);
+    }
+    int cur_lens[2] = {ld.dlens[0], ld.dlens[1]};  // entry lengths of the tile in LDS
     __syncthreads();
+    for (int tile = t0; tile < t1; ++tile) {
+      const int buf = tile & 1;
+      const bool more = tile + 1 < t1;
+      if (more) {
+        ld.fetch_data(tid);                         // tile + 1, lands during this tile's math
+        ld.fetch_pages(a, tile + 2, tid);           // page ids two tiles ahead
+      }
+      compute_tile(lt[buf], lt[buf] + VOFF, cur_lens);
+      // the other buffer was last read in the previous tile, before its barrier
+      if (more) ld.store(lt[buf ^ 1], tid);
+      cur_lens[0] = ld.dlens[0];
+      cur_lens[1] = ld.dlens[1];
+      __syncthreads();
+    }
   }
 
   // Each lane summed P over its own half of the keys (rows 4*hi + ...); both

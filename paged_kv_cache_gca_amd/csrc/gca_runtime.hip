@@ -643,13 +643,16 @@ int gca_read_page(gca_cache* c, int32_t page, void* host_k, void* host_v, gca_st
   GCA_HIP(hipMemcpy(host_k, (char*)c->kpool + off, n * c->esize, hipMemcpyDeviceToHost), "read K page");
   std::vector<char> vt(n * c->esize);
   GCA_HIP(hipMemcpy(vt.data(), (char*)c->vpool + off, n * c->esize, hipMemcpyDeviceToHost), "read V page");
-  // device V page is [H][D][P]; hand it out as [H][P][D]
+  // device V page is [H][D][P] (bf16: slots in operand order, vslot); hand
+  // it out as [H][P][D] in slot order
   char* dst = (char*)host_v;
   for (int h = 0; h < g.H; ++h)
     for (int d = 0; d < g.D; ++d)
-      for (int s = 0; s < g.P; ++s)
+      for (int s = 0; s < g.P; ++s) {
+        const int pos = g.dtype == GCA_BF16 ? gca::vslot(s) : s;
         std::memcpy(dst + (((size_t)h * g.P + s) * g.D + d) * c->esize,
-                    vt.data() + (((size_t)h * g.D + d) * g.P + s) * c->esize, c->esize);
+                    vt.data() + (((size_t)h * g.D + d) * g.P + pos) * c->esize, c->esize);
+      }
   return GCA_OK;
 }
 
