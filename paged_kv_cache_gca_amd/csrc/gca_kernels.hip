@@ -387,10 +387,13 @@ struct Mfma<float> {
 };
 
 // bf16 tiles in LDS: 64 rows of 128 bytes (K: key rows of 64 dims; V^T: dim
-// rows of 64 keys), no padding.  The 16-byte chunk c of row r sits at chunk
-// position c ^ (r & 7) of its row, so the eight rows that one read
-// instruction's lane groups touch hit eight different bank groups.
-__device__ inline int swz(int row, int c) { return row * 128 + ((c ^ (row & 7)) << 4); }
+// rows of 64 keys), no padding.  A 128-bit LDS read serves 16 lanes per
+// cycle from 64 four-byte banks (256 bytes), and an operand read gives those
+// lanes 16 consecutive rows at one logical chunk.  Two consecutive rows span
+// all 64 banks, so the 16-byte chunk c of row r sits at chunk position
+// c ^ ((r >> 1) & 7): the 8 row pairs of a lane group use 8 different
+// positions, each row of a pair its own half of the banks.
+__device__ inline int swz(int row, int c) { return row * 128 + ((c ^ ((row >> 1) & 7)) << 4); }
 
 // K operand: key row `row`, dims [dc*2*KPL + hi*KPL, +KPL).
 __device__ inline bf16x8 read_k(const bf16* lk, int pitch, int row, int dc, int hi) {
@@ -575,14 +578,14 @@ struct DmaLoader {
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int pos = (w * 2 + j) * 64 + lane;        // 16-byte position in the K tile
-      const int r = pos >> 3, c = (pos & 7) ^ (r & 7);  // key row, logical chunk
+      const int r = pos >> 3, c = (pos & 7) ^ ((r >> 1) & 7);  // key row, logical chunk (swz)
       kent[j] = r / P;
       koff[j] = (uint32_t)(((r % P) * kHeadDim + c * 8) * 2);
     }
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int pos = (w * 2 + j) * 64 + lane;        // 16-byte position in the V^T tile
-      const int d = pos >> 3, c = (pos & 7) ^ (d & 7);  // dim row, chunk (8 stored slots)
+      const int d = pos >> 3, c = (pos & 7) ^ ((d >> 1) & 7);  // dim row, chunk (8 stored slots)
       vent[j] = (8 * c) / P;
       voff[j] = (uint32_t)((d * P + (8 * c) % P) * 2);
     }
@@ -878,7 +881,7 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
 #pragma unroll
       for (int i = 0; i < NDC * NQB; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
       }
       if (!sums_ok(ts)) {
         qk_tile(s, true);
@@ -893,7 +896,7 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
 #pragma unroll
       for (int i = 0; i < 2 * NCH * NQB; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
       }
       if (!sums_ok(ts)) {
         seed(1, true, s[1]);
