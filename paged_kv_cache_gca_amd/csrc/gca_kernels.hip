@@ -1034,6 +1034,56 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
   for (int qb = 0; qb < NQB; ++qb) l[qb] += __shfl_xor(l[qb], 32);
 
   // epilogue: O^T accumulators hold dims db*32 + 8*(r/4) + 4*hi + r%4
+  if constexpr (sizeof(T) == 2) {
+    if (a.S > 1) {
+      // split partials go out through LDS (free once every wave is past its
+      // last tile and no tile load is still landing): each wave stages its
+      // 64 queries x 32 dims of one half of the head dim as 128-byte rows
+      // (swizzled like the tiles), then every store instruction writes 8
+      // whole 128-byte lines instead of 32-byte pieces of 32 rows
+      static_assert(NBUF * BUF_ELEMS * sizeof(T) >= kWaves * QPW * 32 * 4, "staging fits the tile buffers");
+      wait_vmem<0>();
+      __syncthreads();
+      char* st = (char*)&lt[0][0] + wave * (QPW * 32 * 4);
+      float inv[NQB];
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) inv[qb] = l[qb] > 0.f ? 1.f / l[qb] : 0.f;
+#pragma unroll
+      for (int db = 0; db < 2; ++db) {
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            floatx4 v;
+            v[0] = o[db][qb][g * 4 + 0] * inv[qb];
+            v[1] = o[db][qb][g * 4 + 1] * inv[qb];
+            v[2] = o[db][qb][g * 4 + 2] * inv[qb];
+            v[3] = o[db][qb][g * 4 + 3] * inv[qb];
+            *(floatx4*)(st + swz(qb * 32 + l32, 2 * g + hi)) = v;
+          }
+        __builtin_amdgcn_wave_barrier();
+        asm volatile("" ::: "memory");
+#pragma unroll
+        for (int it = 0; it < QPW / 8; ++it) {
+          const int row = it * 8 + (lane >> 3), c = lane & 7;
+          const floatx4 v = *(const floatx4*)(st + swz(row, c));
+          const int q = qbase + row;
+          if (q < a.Tq)
+            *(floatx4*)(a.o_part + (((size_t)split * a.Tq + q) * a.H + h) * kHeadDim + db * 32 + c * 4) = v;
+        }
+        __builtin_amdgcn_wave_barrier();
+        asm volatile("" ::: "memory");
+      }
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) {
+        const int q = qbase + qb * 32 + l32;
+        if (q < a.Tq && hi == 0)
+          a.lse_part[((size_t)split * a.Tq + q) * a.H + h] =
+              l[qb] > 0.f ? m[qb] * 0.69314718f + __logf(l[qb]) : -INFINITY;
+      }
+      return;
+    }
+  }
 #pragma unroll
   for (int qb = 0; qb < NQB; ++qb) {
     int q = qbase + qb * 32 + l32;
