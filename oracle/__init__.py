@@ -65,6 +65,8 @@ def lib():
         L.orc_round_bf16.restype = C.c_double
         L.orc_round_bf16.argtypes = [C.c_double]
         L.orc_attend.argtypes = [C.c_void_p, C.c_int64, f32p, i32p, C.c_int32, f64p, f64p, C.c_int32]
+        L.orc_attend_frames.argtypes = [C.c_void_p, C.c_int64, C.c_int32, f32p, i32p, C.c_int32, f64p, f64p,
+                                        C.c_int32]
         L.orc_default_compact.argtypes = [C.c_int32, C.c_int32, C.c_int32, i32p]
         L.orc_default_num_pages.restype = C.c_int64
         L.orc_default_num_pages.argtypes = [C.POINTER(_Cfg)]
@@ -251,4 +253,24 @@ class OracleCache:
                               _p(out, C.c_double), _p(lse, C.c_double), threads)
         if rc != 0:
             raise RuntimeError(f"oracle attend failed: {rc}")
+        return out, lse
+
+    def attend_frames(self, first: int, q: np.ndarray, rows=None, threads: int = 0):
+        """Scale frames together: q [nf][T][H][D] of frames first .. first+nf-1
+        (the last the newest appended frame), each rotated at its own frame
+        index, over the one current context.  Returns out [nf][rows][H][D] and
+        lse [nf][rows][H]."""
+        T, H, D = self.cfg.T, self.cfg.H, self.cfg.D
+        q = np.ascontiguousarray(q, dtype=np.float32)
+        nf = q.shape[0]
+        assert q.shape == (nf, T, H, D)
+        rows = np.arange(T, dtype=np.int32) if rows is None else np.asarray(rows, dtype=np.int32)
+        out = np.zeros((nf, len(rows), H, D), np.float64)
+        lse = np.zeros((nf, len(rows), H), np.float64)
+        if threads <= 0:
+            threads = os.cpu_count() or 1
+        rc = lib().orc_attend_frames(self.h, first, nf, _p(q, C.c_float), _p(rows, C.c_int32), len(rows),
+                                     _p(out, C.c_double), _p(lse, C.c_double), threads)
+        if rc != 0:
+            raise RuntimeError(f"oracle attend_frames failed: {rc}")
         return out, lse

@@ -22,6 +22,11 @@
 //    selected context; the current frame sees all of its own tokens, earlier
 //    frames only through the pools (FAQ "Why are scale frames processed
 //    differently", causal across frames).
+//  * Scale frames: the first few frames are processed together, each one's
+//    queries attending over all of them (bidirectional), before causal
+//    streaming starts (section "Streaming Inference API" and the same FAQ).
+//    Read as: append those frames, then every one of their queries, rotated
+//    at its own frame index, attends over the context that then exists.
 //
 // Readings where the pages are silent (each is a choice, mirrored by the HIP
 // library's own independent code):
@@ -482,23 +487,13 @@ double orc_rope_angle(const orc_config* in, int64_t frame, int32_t tok, int32_t 
 
 double orc_round_bf16(double x) { return round_bf16(x); }
 
-// Attention of frame `frame`'s queries (raw Q [T][H][D]) over the current
-// context, for the query rows listed in `rows`.  Output float64
-// out[n_rows][H][D] and natural-log LSE lse[n_rows][H].
-int orc_attend(void* h, int64_t frame, const float* q, const int32_t* rows, int32_t n_rows,
-               double* out, double* lse, int32_t threads) {
-  Cache& s = *(Cache*)h;
-  if (!s.has_last || frame != s.last_frame) return E_SEQ;
-  if (s.data_less) return E_ARG;
-  const Cfg& c = s.c;
-  long long n = orc_n_ctx(h);
+// Dense softmax attention, float64, of prepared queries Qp [T][H][D] (rows
+// `rows`) over a materialised context K, V [n][H][D]; out[n_rows][H][D],
+// natural-log lse[n_rows][H].
+static void attend_over(const Cfg& c, const std::vector<float>& K, const std::vector<float>& V,
+                        long long n, const std::vector<float>& Qp, const int32_t* rows,
+                        int32_t n_rows, double* out, double* lse, int32_t threads) {
   size_t hd = (size_t)c.H * c.D;
-  // 1. materialise the selected context contiguously
-  std::vector<float> K((size_t)n * hd), V((size_t)n * hd);
-  orc_context(h, K.data(), V.data(), nullptr, nullptr, n);
-  // 2. rotate and round the queries of the listed rows
-  std::vector<float> Qp = prepare(c, frame, q, true);
-  // 3. softmax attention per (row, head), float64
   auto work = [&](int h0, int h1) {
     std::vector<double> sc(n);
     for (int hh = h0; hh < h1; ++hh)
@@ -535,6 +530,49 @@ int orc_attend(void* h, int64_t frame, const float* q, const int32_t* rows, int3
     pool.emplace_back(work, h0, h1);
   }
   for (auto& th : pool) th.join();
+}
+
+// Attention of frame `frame`'s queries (raw Q [T][H][D]) over the current
+// context, for the query rows listed in `rows`.  Output float64
+// out[n_rows][H][D] and natural-log LSE lse[n_rows][H].
+int orc_attend(void* h, int64_t frame, const float* q, const int32_t* rows, int32_t n_rows,
+               double* out, double* lse, int32_t threads) {
+  Cache& s = *(Cache*)h;
+  if (!s.has_last || frame != s.last_frame) return E_SEQ;
+  if (s.data_less) return E_ARG;
+  const Cfg& c = s.c;
+  long long n = orc_n_ctx(h);
+  size_t hd = (size_t)c.H * c.D;
+  // 1. materialise the selected context contiguously
+  std::vector<float> K((size_t)n * hd), V((size_t)n * hd);
+  orc_context(h, K.data(), V.data(), nullptr, nullptr, n);
+  // 2. rotate and round the queries
+  std::vector<float> Qp = prepare(c, frame, q, true);
+  // 3. softmax attention per (row, head), float64
+  attend_over(c, K, V, n, Qp, rows, n_rows, out, lse, threads);
+  return OK;
+}
+
+// Scale frames processed together: the queries of frames first .. first +
+// nf - 1 (raw Q [nf][T][H][D], the last of them the newest appended frame),
+// each rotated at its own frame index, attend over the one current context.
+// out[nf][n_rows][H][D], lse[nf][n_rows][H].
+int orc_attend_frames(void* h, int64_t first, int32_t nf, const float* q, const int32_t* rows,
+                      int32_t n_rows, double* out, double* lse, int32_t threads) {
+  Cache& s = *(Cache*)h;
+  if (first < 0 || nf < 1) return E_ARG;
+  if (!s.has_last || first + nf - 1 != s.last_frame) return E_SEQ;
+  if (s.data_less) return E_ARG;
+  const Cfg& c = s.c;
+  long long n = orc_n_ctx(h);
+  size_t hd = (size_t)c.H * c.D;
+  std::vector<float> K((size_t)n * hd), V((size_t)n * hd);
+  orc_context(h, K.data(), V.data(), nullptr, nullptr, n);
+  for (int i = 0; i < nf; ++i) {
+    std::vector<float> Qp = prepare(c, first + i, q + (size_t)i * c.T * hd, true);
+    attend_over(c, K, V, n, Qp, rows, n_rows, out + (size_t)i * n_rows * hd,
+                lse ? lse + (size_t)i * n_rows * c.H : nullptr, threads);
+  }
   return OK;
 }
 

@@ -521,3 +521,79 @@ def test_page_contents_match_context_rows():
         np.testing.assert_array_equal(v[:, :l].transpose(1, 0, 2), vc[r:r + l])
         r += l
     assert r == n
+
+
+# --------------------------------------------------------------------------- scale frames
+
+
+def _scale_cache(A, dtype, rope, seed=7, T=18, H=2, D=64):
+    cfg = oracle.OracleConfig(T=T, H=H, D=D, P=8, dtype=dtype, A=A, W=2, C=2, compact_idx=[0, 5],
+                              rope=rope, num_special=2, grid_h=4, grid_w=4, max_frames=12)
+    fs = FrameStream(seed, T, H, D, dtype)
+    c = oracle.OracleCache(cfg)
+    for f in range(A):
+        k, v = fs.kv(f)
+        assert c.append(f, k, v) == 0 and c.evict() == 0
+    return cfg, fs, c
+
+
+@pytest.mark.parametrize("A,nf,dtype,rope", [(3, 3, "f32", 1), (4, 4, "bf16", 1), (4, 2, "bf16", 1),
+                                              (2, 2, "f32", 0)])
+def test_scale_frames_match_bruteforce_bidirectional(A, nf, dtype, rope):
+    """The scale frames' queries (each rotated at its own frame index) attend over every
+    token of all A appended frames, later frames included; dense attention built here."""
+    T, H, D = 18, 2, 64
+    cfg, fs, c = _scale_cache(A, dtype, rope)
+    first = A - nf
+    q = np.stack([fs.q(first + i) for i in range(nf)])
+    o, lse = c.attend_frames(first, q)
+    K, V = [], []
+    for f in range(A):
+        k, v = fs.kv(f)
+        kp = oracle.rope(cfg, f, k) if rope else k.astype(np.float64)
+        kp = round64_bf16(kp) if dtype == "bf16" else kp.astype(np.float32).astype(np.float64)
+        K.append(kp)
+        V.append(v.astype(np.float64))
+    K, V = np.concatenate(K), np.concatenate(V)
+    assert c.n_ctx() == A * T
+    for i in range(nf):
+        qp = oracle.rope(cfg, first + i, q[i]) if rope else q[i].astype(np.float64)
+        qp = round64_bf16(qp) if dtype == "bf16" else qp.astype(np.float32).astype(np.float64)
+        o_ref, lse_ref = _sdpa64(qp, K, V, D ** -0.5)
+        np.testing.assert_allclose(o[i], o_ref, rtol=0, atol=1e-12)
+        np.testing.assert_allclose(lse[i], lse_ref, rtol=0, atol=1e-12)
+
+
+def test_scale_frames_one_frame_is_attend_and_closed_forms():
+    A, T, H, D = 3, 18, 2, 64
+    cfg, fs, c = _scale_cache(A, "bf16", 1)
+    # one frame: exactly the single-frame attention of the newest frame
+    o1, l1 = c.attend_frames(A - 1, fs.q(A - 1)[None])
+    o, lse = c.attend(A - 1, fs.q(A - 1))
+    assert np.array_equal(o1[0], o) and np.array_equal(l1[0], lse)
+    # K = 0 (float32 storage): every scale frame's output is the mean of V over all of them
+    cfg, _, _ = _scale_cache(A, "f32", 1)
+    c0 = oracle.OracleCache(cfg)
+    rng = np.random.default_rng(3)
+    vs = [rng.standard_normal((T, H, D)).astype(np.float32) for _ in range(A)]
+    for f in range(A):
+        assert c0.append(f, np.zeros((T, H, D), np.float32), vs[f]) == 0 and c0.evict() == 0
+    q = rng.standard_normal((A, T, H, D)).astype(np.float32)
+    o0, l0 = c0.attend_frames(0, q)
+    mean = np.concatenate(vs).astype(np.float64).mean(0)
+    np.testing.assert_allclose(o0, np.broadcast_to(mean, o0.shape), atol=1e-13)
+    np.testing.assert_allclose(l0, math.log(A * T), atol=1e-13)
+    # the first frame's output changes with the last frame's values (bidirectional)
+    c2 = oracle.OracleCache(cfg)
+    for f in range(A):
+        assert c2.append(f, np.zeros((T, H, D), np.float32), vs[f] + (f == A - 1)) == 0
+    o2, _ = c2.attend_frames(0, q)
+    np.testing.assert_allclose(o2[0] - o0[0], 1.0 / A, atol=1e-13)
+
+
+def test_scale_frames_sequence_errors():
+    cfg, fs, c = _scale_cache(3, "f32", 0)
+    q = np.stack([fs.q(f) for f in range(3)])
+    for first, qq in [(1, q), (0, q[:2]), (-1, q[:1])]:
+        with pytest.raises(RuntimeError):
+            c.attend_frames(first, qq)
