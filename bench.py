@@ -44,6 +44,8 @@ def parse():
     ap.add_argument("--workload", default="bf16_T1004_H16_P16_W16_64f")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=64)
+    ap.add_argument("--no-scale-phase", action="store_true",
+                    help="skip the scale-phase measurement (counter runs that average per stream launch)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 256 MiB device-to-device copy (counter calibration)")
     return ap.parse_args()
@@ -215,6 +217,100 @@ def run_gpu(w, steps, warmup):
                 tail_frames=(f_tail, w.n_frames), device=device)
 
 
+def run_scale_phase(w, nf=8, reps=10, warmup=2):
+    """The stream's first phase: nf scale frames appended as the anchor, then all
+    of their queries in one joint (bidirectional) attention call.  HIP events
+    from the library around the attention launch; events on the stream around
+    each whole phase (nf appends + the joint call)."""
+    import torch
+
+    from paged_kv_cache_gca_amd import gca
+    from paged_kv_cache_gca_amd.synth import FrameStream
+
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    fs = FrameStream(w.seed, w.T, w.H, w.D, w.dtype, n_base=w.n_base)
+    K, V = [], []
+    for f in range(nf):
+        k, v = fs.kv(f)
+        K.append(torch.from_numpy(k).to(dt).cuda())
+        V.append(torch.from_numpy(v).to(dt).cuda())
+    Q = torch.stack([torch.from_numpy(fs.q(f)).to(dt) for f in range(nf)]).cuda()
+    cache = gca.Cache(gca.Config.from_workload(w, num_anchor_frames=nf))
+    out = torch.empty((nf, w.T, w.H, w.D), dtype=torch.float32, device="cuda")
+    lse = torch.empty((nf, w.T, w.H), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def phase():
+        if cache.reset(stream) != 0:
+            raise RuntimeError("reset failed")
+        for f in range(nf):
+            if cache.append_frame(f, K[f], V[f], stream=stream) != 0 or cache.evict_compact(stream) != 0:
+                raise RuntimeError("scale-frame append failed")
+        if cache.attend_frames(0, Q, out, lse, stream=stream) != 0:
+            raise RuntimeError("joint attention failed")
+
+    for _ in range(warmup):
+        phase()
+    torch.cuda.synchronize()
+    n_ctx = cache.query().n_ctx
+    cache.profile_enable(reps + 4, kinds=("attn",))
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for e0, e1 in ev:
+        e0.record(stream)
+        phase()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    attn_ms, n = cache.profile_read("attn")
+    cache.profile_enable(0)
+    cache.close()
+    assert torch.isfinite(out).all()
+    phase_ms = sum(e0.elapsed_time(e1) for e0, e1 in ev) / reps
+    flop = 4.0 * nf * w.T * n_ctx * w.H * w.D
+    us = attn_ms * 1e3 / max(n, 1)
+    tflops = flop / (us * 1e-6) / 1e12
+    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_MFMA_TFLOPS
+    return {"frames": nf, "queries": nf * w.T, "n_ctx": n_ctx, "attn_us": round(us, 2),
+            "attn_flop": flop, "achieved": round(tflops, 1), "peak": peak, "unit": "TFLOP/s",
+            "frac": round(tflops / peak, 4), "phase_us": round(phase_ms * 1e3, 1),
+            "timing": f"{reps} phases after {warmup} warm-up: library HIP events around the joint "
+                      "attention launch; stream events around each phase (appends + joint call)"}
+
+
+def scale_phase_cpu(w, nf=8, n_rows=8):
+    """The oracle on the scale phase (test infrastructure): nf appends, then the
+    joint attention for n_rows of the T query rows of every frame (and 1 row,
+    to separate the fixed cost), full-row time scaled linearly in rows."""
+    import numpy as np
+
+    import oracle
+    from paged_kv_cache_gca_amd.synth import FrameStream
+
+    threads = os.cpu_count() or 1
+    fs = FrameStream(w.seed, w.T, w.H, w.D, w.dtype, n_base=w.n_base)
+    cfg = oracle.OracleConfig(T=w.T, H=w.H, D=w.D, P=w.P, dtype=w.dtype, A=nf, W=w.W, C=w.C,
+                              rope=w.rope, num_special=w.num_special, grid_h=w.grid_h,
+                              grid_w=w.grid_w, max_frames=w.n_frames)
+    c = oracle.OracleCache(cfg)
+    rows = np.linspace(0, w.T - 1, n_rows).astype(np.int32)
+    a = time.perf_counter()
+    for f in range(nf):
+        k, v = fs.kv(f)
+        c.append(f, k, v)
+        c.evict()
+    b = time.perf_counter()
+    q = np.stack([fs.q(f) for f in range(nf)])
+    c.attend_frames(0, q, rows=rows[:1], threads=threads)
+    m = time.perf_counter()
+    c.attend_frames(0, q, rows=rows, threads=threads)
+    e = time.perf_counter()
+    one = m - b
+    per_row = max(0.0, (e - m) - one) / max(1, n_rows - 1)
+    est = (b - a) + one + per_row * w.T
+    return {"us": round(est * 1e6, 1), "cores": threads, "kind": "oracle",
+            "sample": f"{nf} appends plus the joint attention for {n_rows} of {w.T} query rows per frame "
+                      f"(and 1 row), full-row time scaled linearly in rows"}
+
+
 def append_compact_line(w, kern):
     """HBM roofline of the append and compaction launches (algorithmic bytes per launch)."""
     esize = 2 if w.dtype == "bf16" else 4
@@ -343,9 +439,14 @@ def main():
         "kernel_hash": kh,
         "device": r["device"],
     }
+    if w.rope and w.dtype == "bf16" and not args.no_scale_phase:
+        print("[bench] scale phase", file=sys.stderr, flush=True)
+        line["scale_phase"] = run_scale_phase(w)
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         line["cpu_baseline"] = run_cpu_baseline(w, args.cpu_rows)
+        if "scale_phase" in line:
+            line["scale_phase"]["cpu_baseline"] = scale_phase_cpu(w, line["scale_phase"]["frames"])
     print(json.dumps(line), flush=True)
 
 

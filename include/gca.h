@@ -176,6 +176,24 @@ int gca_evict_compact(gca_cache* cache, gca_stream_t stream);
 int gca_attend(gca_cache* cache, int64_t frame_idx, const void* q, void* out, float* lse,
                gca_stream_t stream);
 
+/* Scale frames processed together: a stream starts with a few frames that are
+ * handled jointly, each attending over all of them (bidirectional), before
+ * causal streaming begins ("How the Geometric Context Transformer Enables
+ * Streaming 3D Reconstruction in LingBot-Map", section "Streaming Inference
+ * API" and the FAQ on why scale frames are processed differently).  Appended
+ * as the anchor frames, they are attended to here in one call:
+ * compute_attention for the queries of the n_frames frames first_frame ..
+ * first_frame + n_frames - 1, q raw [n_frames][T][H][D], each frame's queries
+ * rotated at its own frame index (rope = 1), all over the one current context
+ * (the gather list of gca_attend).  out [n_frames][T][H][D] (out_dtype), lse
+ * [n_frames][T][H] or NULL.  The last of the frames must be the last appended
+ * frame, as for gca_attend; n_frames = 1 is gca_attend.  Errors:
+ * INVALID_ARGUMENT (null/misaligned, first_frame < 0, n_frames < 1); CAPACITY
+ * (n_frames above max(1, num_anchor_frames), the frames the query workspace
+ * holds); SEQUENCE. */
+int gca_attend_frames(gca_cache* cache, int64_t first_frame, int32_t n_frames, const void* q,
+                      void* out, float* lse, gca_stream_t stream);
+
 /* rollback_last_frame(global_idx): drop the pending GCA_APPEND_TEMP frame and
  * return its pages to the ring head; the cache is as before its append.
  * Errors: SEQUENCE (no TEMP pending or another frame index). */

@@ -114,9 +114,10 @@ struct MergeArgs {
 __host__ __device__ inline int vslot(int s) { return (s & ~12) | ((s & 4) << 1) | ((s & 8) >> 1); }
 
 struct RopeArgs {
-  const void* x;
+  const void* x;  // [nf][T][H][D]: frames frame, frame + 1, ..., frame + nf - 1
   void* y;
   int64_t frame;
+  int nf;
   int T, H;
   int rotate;   // 0: y = scale * x (no rotation)
   float scale;  // 1 for keys; sm_scale * log2(e) for the attention's queries

@@ -86,14 +86,15 @@ template <typename T>
 __device__ inline void rope_chunk(const RopeArgs& a, size_t c) {
   constexpr int EPC = 16 / sizeof(T);
   constexpr int CPR = kHeadDim / EPC;
-  size_t total = (size_t)a.T * a.H * CPR;
+  size_t total = (size_t)a.nf * a.T * a.H * CPR;
   if (c >= total) return;
   int part = (int)(c % CPR);
-  int tok = (int)(c / CPR / a.H);
+  int row = (int)(c / CPR / a.H);  // token of the nf stacked frames
+  int tok = row % a.T;
   Vec16<T> v;
   v.u = ((const uint4*)a.x)[c];
   if (a.rotate) {
-    rotate_chunk<T>(v, a.tabs, a.frame, tok, part * EPC / 2, a.scale);
+    rotate_chunk<T>(v, a.tabs, a.frame + row / a.T, tok, part * EPC / 2, a.scale);
   } else {
 #pragma unroll
     for (int i = 0; i < EPC; ++i) v.e[i] = from_f<T>(to_f(v.e[i]) * a.scale);
@@ -102,7 +103,7 @@ __device__ inline void rope_chunk(const RopeArgs& a, size_t c) {
 }
 template <typename T>
 inline size_t rope_chunks(const RopeArgs& a) {
-  return (size_t)a.T * a.H * (kHeadDim / (16 / sizeof(T)));
+  return (size_t)a.nf * a.T * a.H * (kHeadDim / (16 / sizeof(T)));
 }
 
 template <typename T>
@@ -1212,7 +1213,7 @@ hipError_t launch_update(int dtype, const AppendArgs* ap, const EvictArgs* ev, c
 
 hipError_t launch_prepare(int dtype, const SelectArgs& sa, const RopeArgs& ra, hipStream_t s) {
   int sel_blocks = (sa.n_write + 255) / 256;
-  size_t chunks = (size_t)ra.T * ra.H * (dtype ? 8 : 16);
+  size_t chunks = dtype ? rope_chunks<bf16>(ra) : rope_chunks<float>(ra);
   int rope_blocks = (int)((chunks + 255) / 256);
   dim3 grid(sel_blocks + rope_blocks);
   if (dtype) hipLaunchKernelGGL(k_prepare<bf16>, grid, dim3(256), 0, s, sa, ra, sel_blocks);
@@ -1242,7 +1243,7 @@ hipError_t launch_merge(const MergeArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_rope(int dtype, const RopeArgs& a, hipStream_t s) {
-  size_t chunks = (size_t)a.T * a.H * (dtype ? 8 : 16);
+  size_t chunks = dtype ? rope_chunks<bf16>(a) : rope_chunks<float>(a);
   dim3 grid((unsigned)((chunks + 255) / 256));
   if (dtype) hipLaunchKernelGGL(k_rope<bf16>, grid, dim3(256), 0, s, a);
   else hipLaunchKernelGGL(k_rope<float>, grid, dim3(256), 0, s, a);

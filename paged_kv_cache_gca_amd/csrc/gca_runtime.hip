@@ -223,11 +223,12 @@ gca::EvictArgs evict_args(gca_cache* c, const gca::EvictStep& st) {
 
 // The attention's queries: rotated when rope = 1 and scaled by
 // sm_scale * log2(e), rounded once, into the query workspace.
-gca::RopeArgs query_args(gca_cache* c, int64_t frame_idx, const void* q) {
+gca::RopeArgs query_args(gca_cache* c, int64_t frame_idx, const void* q, int nf = 1) {
   gca::RopeArgs ra;
   ra.x = q;
   ra.y = c->qrot;
   ra.frame = frame_idx;
+  ra.nf = nf;
   ra.T = c->g.T;
   ra.H = c->g.H;
   ra.rotate = c->g.rope;
@@ -236,19 +237,21 @@ gca::RopeArgs query_args(gca_cache* c, int64_t frame_idx, const void* q) {
   return ra;
 }
 
-// Attention over the gather list already built for `st` (queries qa already
-// prepared by query_args), then the split merge.
+// Attention over the gather list already built for `st` (queries qa of nf
+// stacked frames already prepared by query_args), then the split merge.
 int attend_launch(gca_cache* c, int64_t frame_idx, const void* qa, void* out, float* lse,
-                  const gca::SelectStep& st, hipStream_t s) {
+                  const gca::SelectStep& st, hipStream_t s, int nf = 1) {
   const gca::Geometry& g = c->g;
+  const int Tq = nf * g.T;
   int ept = gca::kKeysPerTile / g.P;
   int n_tiles = (st.n_sel + ept - 1) / ept;
   int qpw = gca::queries_per_wg(g.dtype);
-  int qtiles = (g.T + qpw - 1) / qpw;
-  // split the context so that about two workgroups run per compute unit
+  int qtiles = (Tq + qpw - 1) / qpw;
+  // split the context so that about two workgroups run per compute unit; the
+  // split workspace holds kMaxSplits partials of one frame's rows
   int base = qtiles * g.H;
   int S = (2 * c->num_cu + base - 1) / base;
-  S = std::min(S, kMaxSplits);
+  S = std::min(S, kMaxSplits / nf);
   S = std::min(S, std::max(1, n_tiles / 2));
   S = std::max(S, 1);
   int tps = (n_tiles + S - 1) / S;
@@ -264,7 +267,7 @@ int attend_launch(gca_cache* c, int64_t frame_idx, const void* qa, void* out, fl
   a.out = out;
   a.lse = lse;
   a.frame = frame_idx;
-  a.Tq = g.T;
+  a.Tq = Tq;
   a.H = g.H;
   a.P = g.P;
   a.n_sel = st.n_sel;
@@ -296,7 +299,7 @@ int attend_launch(gca_cache* c, int64_t frame_idx, const void* qa, void* out, fl
     m.lse_part = c->lse_part;
     m.out = out;
     m.lse = lse;
-    m.rows = g.T * g.H;
+    m.rows = Tq * g.H;
     m.S = S;
     m.out_bf16 = a.out_bf16;
     Prof p(c, 4, s);
@@ -375,7 +378,8 @@ int gca_cache_create(const gca_config* cfg, gca_cache** out) {
     return fail(e, "hipMalloc split workspace");
   if ((e = dmalloc(&c->lse_part, sizeof(float) * rows * kMaxSplits)) != hipSuccess)
     return fail(e, "hipMalloc split workspace");
-  if ((e = dmalloc(&c->qrot, rows * g.D * c->esize)) != hipSuccess)
+  // prepared queries: one frame, or the A anchor frames of a joint call
+  if ((e = dmalloc(&c->qrot, rows * g.D * c->esize * std::max(1, g.A))) != hipSuccess)
     return fail(e, "hipMalloc query workspace");
   if ((e = hipMemset(c->kpool, 0, pool_bytes)) != hipSuccess) return fail(e, "hipMemset K pool");
   if ((e = hipMemset(c->vpool, 0, pool_bytes)) != hipSuccess) return fail(e, "hipMemset V pool");
@@ -500,6 +504,28 @@ int gca_attend(gca_cache* c, int64_t frame_idx, const void* q, void* out, float*
   return attend_launch(c, frame_idx, c->qrot, out, lse, st, s);
 }
 
+int gca_attend_frames(gca_cache* c, int64_t first_frame, int32_t n_frames, const void* q, void* out,
+                      float* lse, gca_stream_t stream) {
+  if (!c || !aligned16(q) || !aligned16(out) || (lse && ((uintptr_t)lse & 3)) || first_frame < 0 ||
+      n_frames < 1)
+    return GCA_ERR_INVALID_ARGUMENT;
+  if (n_frames > std::max(1, c->g.A)) return GCA_ERR_CAPACITY;
+  int rc = c->plan.check_attend(first_frame + n_frames - 1);
+  if (rc) return rc;
+  hipStream_t s = (hipStream_t)stream;
+  const gca::Geometry& g = c->g;
+  gca::SelectStep st = c->plan.select();
+  {
+    Prof p(c, 2, s);
+    GCA_HIP(gca::launch_prepare(g.dtype, select_args(c, st), query_args(c, first_frame, q, n_frames), s),
+            "prepare kernel launch");
+  }
+  c->sel_valid = true;
+  c->sel_n = st.n_sel;
+  c->sel_ctx = st.n_ctx;
+  return attend_launch(c, first_frame + n_frames - 1, c->qrot, out, lse, st, s, n_frames);
+}
+
 int gca_rollback_last_frame(gca_cache* c, int64_t frame_idx, gca_stream_t stream) {
   (void)stream;
   if (!c) return GCA_ERR_INVALID_ARGUMENT;
@@ -579,6 +605,7 @@ int gca_rope3d(gca_cache* c, int64_t frame_idx, const void* x, void* y, gca_stre
   a.x = x;
   a.y = y;
   a.frame = frame_idx;
+  a.nf = 1;
   a.T = c->g.T;
   a.H = c->g.H;
   a.rotate = 1;

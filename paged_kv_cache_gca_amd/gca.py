@@ -79,6 +79,7 @@ def _load():
         "gca_append_frame": [vp, i64, vp, vp, u32, vp],
         "gca_evict_compact": [vp, vp],
         "gca_attend": [vp, i64, vp, vp, vp, vp],
+        "gca_attend_frames": [vp, i64, i32, vp, vp, vp, vp],
         "gca_rollback_last_frame": [vp, i64, vp],
         "gca_step": [vp, i64, vp, vp, vp, vp, vp, u32, vp],
         "gca_select": [vp, vp],
@@ -265,6 +266,11 @@ class Cache:
 
     def attend(self, frame: int, q, out, lse=None, stream=None) -> int:
         return _lib.gca_attend(self.h, frame, _ptr(q), _ptr(out), _ptr(lse), _stream(stream))
+
+    def attend_frames(self, first: int, q, out, lse=None, stream=None) -> int:
+        """scale frames together: q [n][T][H][D] of frames first .. first+n-1"""
+        return _lib.gca_attend_frames(self.h, first, int(q.shape[0]), _ptr(q), _ptr(out), _ptr(lse),
+                                      _stream(stream))
 
     def rollback_last_frame(self, frame: int, stream=None) -> int:
         return _lib.gca_rollback_last_frame(self.h, frame, _stream(stream))

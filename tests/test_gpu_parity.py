@@ -492,3 +492,79 @@ def _lib_step(c, frame, k, v, q, out, flags=1, q_offset=0):
     return g._lib.gca_step(c.h, frame, ctypes.c_void_p(k.data_ptr()), ctypes.c_void_p(v.data_ptr()),
                            ctypes.c_void_p(q.data_ptr() + q_offset), ctypes.c_void_p(out.data_ptr()),
                            None, flags, None)
+
+
+# --------------------------------------------------------------------------- scale frames
+
+
+def _scale_pair(T, H, P, dtype, A, rope, ns, gh, gw, seed=43):
+    w = WL.Workload("scale", T=T, H=H, D=64, P=P, dtype=dtype, n_frames=A + 2, A=A, W=2, C=3,
+                    rope=rope, num_special=ns, grid_h=gh, grid_w=gw, seed=seed)
+    p = Pair(w)
+    for f in range(A):
+        p.step(f)
+    return p
+
+
+def _attend_frames(p, first, nf):
+    w = p.w
+    q = np.stack([p.fs.q(first + i) for i in range(nf)])
+    out = torch.empty((nf, w.T, w.H, w.D), dtype=torch.float32, device="cuda")
+    lse = torch.empty((nf, w.T, w.H), dtype=torch.float32, device="cuda")
+    assert p.gpu.attend_frames(first, dev(q, w.dtype), out, lse) == 0
+    return q, out, lse
+
+
+@pytest.mark.parametrize("T,H,P,dtype,A,nf,rope,ns,gh,gw,sampled", [
+    (64, 2, 16, "f32", 3, 3, 0, 0, 8, 8, False),         # fp32, every row
+    (300, 4, 16, "bf16", 4, 4, 1, 3, 9, 33, False),      # several q tiles, ragged tail
+    (300, 4, 64, "bf16", 4, 2, 1, 3, 9, 33, False),      # the last two of four anchors
+    (1004, 16, 16, "bf16", 8, 8, 1, 5, 27, 37, True),    # 8 scale frames at the frame shape
+    (1004, 16, 64, "bf16", 4, 4, 1, 5, 27, 37, True),
+])
+def test_scale_frames_joint_attention_parity(T, H, P, dtype, A, nf, rope, ns, gh, gw, sampled):
+    """The anchors' queries in one call, each frame rotated at its own index, over the
+    context of all anchors (bidirectional), against the oracle frame by frame; then
+    the stream goes on causally over that anchor."""
+    p = _scale_pair(T, H, P, dtype, A, rope, ns, gh, gw)
+    first = A - nf
+    rows = (np.unique(np.r_[np.arange(0, T, 61), 255, 256, T - 1]).astype(np.int32) if sampled
+            else np.arange(T, dtype=np.int32))
+    q, out, lse = _attend_frames(p, first, nf)
+    o_ref, lse_ref = p.orc.attend_frames(first, q, rows=rows)
+    for i in range(nf):
+        o = out[i].cpu().numpy()[rows].astype(np.float64)
+        l = lse[i].cpu().numpy()[rows].astype(np.float64)
+        assert np.isfinite(o).all()
+        err = float(np.abs(o - o_ref[i]).max())
+        assert err <= TOL[dtype], (i, err)
+        bound = LSE_TOL[dtype] + query_rounding_bound(p, first + i, q[i], rows)
+        assert (np.abs(l - lse_ref[i]) <= bound).all(), i
+    p.check_state()
+    if not sampled:
+        for f in range(A, A + 2):
+            p.step(f)
+            _cmp_attention(p, f)
+
+
+def test_scale_frames_one_frame_is_attend_bitwise():
+    p = _scale_pair(300, 4, 16, "bf16", 3, 1, 3, 9, 33, seed=44)
+    q, out, lse = _attend_frames(p, 2, 1)
+    _, out1, lse1 = p.attend_gpu(2, q[0])
+    assert torch.equal(out[0], out1) and torch.equal(lse[0], lse1)
+
+
+def test_scale_frames_errors_change_nothing():
+    g = gca()
+    p = _scale_pair(64, 2, 16, "f32", 3, 0, 0, 8, 8, seed=45)
+    before = p.gpu.export_state()
+    w = p.w
+    q4 = torch.zeros((4, w.T, w.H, w.D), dtype=torch.float32, device="cuda")
+    out = torch.empty_like(q4)
+    assert p.gpu.attend_frames(0, q4, out) == g.GCA_ERR_CAPACITY        # more frames than anchors
+    assert p.gpu.attend_frames(1, q4[:3], out) == g.GCA_ERR_SEQUENCE    # 1..3: 3 not appended
+    assert p.gpu.attend_frames(-1, q4[:1], out) == g.GCA_ERR_INVALID_ARGUMENT
+    assert p.gpu.attend_frames(0, q4[:0], out) == g.GCA_ERR_INVALID_ARGUMENT
+    after = p.gpu.export_state()
+    for key in ("free", "frame_idx", "frame_pages", "traj_pages"):
+        np.testing.assert_array_equal(before[key], after[key])
