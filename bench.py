@@ -44,8 +44,9 @@ def parse():
     ap.add_argument("--workload", default="bf16_T1004_H16_P16_W16_64f")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=64)
-    ap.add_argument("--no-scale-phase", action="store_true",
-                    help="skip the scale-phase measurement (counter runs that average per stream launch)")
+    ap.add_argument("--stream-only", action="store_true",
+                    help="skip the scale-phase and camera-head measurements (counter runs that "
+                         "average per stream launch)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 256 MiB device-to-device copy (counter calibration)")
     return ap.parse_args()
@@ -289,7 +290,7 @@ def scale_phase_cpu(w, nf=8, n_rows=8):
     fs = FrameStream(w.seed, w.T, w.H, w.D, w.dtype, n_base=w.n_base)
     cfg = oracle.OracleConfig(T=w.T, H=w.H, D=w.D, P=w.P, dtype=w.dtype, A=nf, W=w.W, C=w.C,
                               rope=w.rope, num_special=w.num_special, grid_h=w.grid_h,
-                              grid_w=w.grid_w, max_frames=w.n_frames)
+                              grid_w=w.grid_w, rope_theta=w.rope_theta, max_frames=w.n_frames)
     c = oracle.OracleCache(cfg)
     rows = np.linspace(0, w.T - 1, n_rows).astype(np.int32)
     a = time.perf_counter()
@@ -309,6 +310,23 @@ def scale_phase_cpu(w, nf=8, n_rows=8):
     return {"us": round(est * 1e6, 1), "cores": threads, "kind": "oracle",
             "sample": f"{nf} appends plus the joint attention for {n_rows} of {w.T} query rows per frame "
                       f"(and 1 row), full-row time scaled linearly in rows"}
+
+
+def camera_line(wc, steps=3, warmup=1):
+    """The causal camera head's cache: one token per frame, one query row per
+    head; every step is launch-latency bound, so the figure is per frame."""
+    r = run_gpu(wc, steps, warmup)
+    attn_ms, n = r["kern"]["attn"]
+    us = attn_ms * 1e3 / max(n, 1)
+    esize = 2 if wc.dtype == "bf16" else 4
+    mean_ctx = sum(r["n_ctx"]) / len(r["n_ctx"])
+    kv = 2 * mean_ctx * wc.H * wc.D * esize  # K and V of the mean context, read once
+    return {"workload": wc.name, "value": round(steps * wc.n_frames / r["seconds"], 1),
+            "unit": "frames/s", "us_per_frame": round(r["seconds"] * 1e6 / (steps * wc.n_frames), 2),
+            "attn_us": round(us, 2), "mean_n_ctx": round(mean_ctx, 1), "attn_bytes": round(kv),
+            "attn_gbs": round(kv / (us * 1e-6) / 1e9, 1), "bound": "latency",
+            "timing": f"{steps} streams of {wc.n_frames} frames after {warmup} warm-up (gca_step per frame); "
+                      "library HIP events around each attention launch"}
 
 
 def append_compact_line(w, kern):
@@ -345,7 +363,7 @@ def run_cpu_baseline(w, rows_per_frame):
     fs = FrameStream(w.seed, w.T, w.H, w.D, w.dtype, n_base=w.n_base, drift_sigma=w.drift_sigma)
     cfg = oracle.OracleConfig(T=w.T, H=w.H, D=w.D, P=w.P, dtype=w.dtype, A=w.A, W=w.W, C=w.C,
                               rope=w.rope, num_special=w.num_special, grid_h=w.grid_h,
-                              grid_w=w.grid_w, max_frames=w.n_frames)
+                              grid_w=w.grid_w, rope_theta=w.rope_theta, max_frames=w.n_frames)
     c = oracle.OracleCache(cfg)
     rows = np.linspace(0, w.T - 1, rows_per_frame).astype(np.int32)
     n_frames = min(w.n_frames, 64)
@@ -439,14 +457,18 @@ def main():
         "kernel_hash": kh,
         "device": r["device"],
     }
-    if w.rope and w.dtype == "bf16" and not args.no_scale_phase:
+    if w.rope and w.dtype == "bf16" and not args.stream_only:
         print("[bench] scale phase", file=sys.stderr, flush=True)
         line["scale_phase"] = run_scale_phase(w)
+        print("[bench] camera-head cache", file=sys.stderr, flush=True)
+        line["camera_head"] = camera_line(WL.CAMERA_T1)
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         line["cpu_baseline"] = run_cpu_baseline(w, args.cpu_rows)
         if "scale_phase" in line:
             line["scale_phase"]["cpu_baseline"] = scale_phase_cpu(w, line["scale_phase"]["frames"])
+        if "camera_head" in line:
+            line["camera_head"]["cpu_baseline"] = run_cpu_baseline(WL.CAMERA_T1, 1)
     print(json.dumps(line), flush=True)
 
 

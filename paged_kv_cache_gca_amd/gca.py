@@ -180,7 +180,7 @@ class Config:
     def from_workload(w, **kw) -> "Config":
         d = dict(tokens_per_frame=w.T, num_heads=w.H, head_dim=w.D, page_size=w.P, dtype=w.dtype,
                  num_anchor_frames=w.A, window_frames=w.W, num_compact=w.C, rope=w.rope,
-                 num_special=w.num_special, grid_h=w.grid_h, grid_w=w.grid_w,
+                 num_special=w.num_special, grid_h=w.grid_h, grid_w=w.grid_w, rope_theta=w.rope_theta,
                  max_frames=w.n_frames)
         d.update(kw)
         return Config(**d)

@@ -34,6 +34,7 @@ class Workload:
     n_base: int | None = None      # distinct base frames cycled (None: every frame distinct)
     drift_sigma: float = 0.0
     seed: int = 1
+    rope_theta: float = 10000.0
 
     @property
     def n_keyframes(self) -> int:
@@ -63,4 +64,11 @@ RING20K_W12 = Workload("bf16_T1004_H16_P64_ring12_20000f", T=1004, H=16, D=64, P
                        dtype="bf16", n_frames=20000, A=0, W=12, C=0, rope=1, num_special=5,
                        grid_h=27, grid_w=37, n_base=64, seed=5)
 
-ALL = [TINY_F32, FRAME1004_W16, STREAM1000_W64, STREAM10K_KF4, RING20K_W12]
+# The causal camera head's own cache: one camera token per frame under the same
+# pool policy (anchor, sliding window, kept tokens of evicted frames) with its
+# own rotary base; a decode-shaped attention (one query row per head).
+CAMERA_T1 = Workload("bf16_T1_H16_P16_W32_camera_1000f", T=1, H=16, D=64, P=16, dtype="bf16",
+                     n_frames=1000, A=1, W=32, C=1, rope=1, num_special=0, grid_h=1, grid_w=1,
+                     n_base=64, seed=6, rope_theta=100.0)
+
+ALL = [TINY_F32, FRAME1004_W16, STREAM1000_W64, STREAM10K_KF4, RING20K_W12, CAMERA_T1]

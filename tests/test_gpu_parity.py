@@ -239,8 +239,8 @@ def test_ring20k_tail_sampled():
     _cmp_attention(p, 19999, rows)
 
 
-@pytest.mark.parametrize("w", [WL.FRAME1004_W16, WL.STREAM1000_W64, WL.STREAM10K_KF4, WL.RING20K_W12],
-                         ids=lambda w: w.name)
+@pytest.mark.parametrize("w", [WL.FRAME1004_W16, WL.STREAM1000_W64, WL.STREAM10K_KF4, WL.RING20K_W12,
+                               WL.CAMERA_T1], ids=lambda w: w.name)
 def test_fullsize_bookkeeping_every_step(w):
     """Ring, page tables and gather list bit-exact at every step of the whole stream."""
     p = Pair(w, data=False)
@@ -251,6 +251,22 @@ def test_fullsize_bookkeeping_every_step(w):
             p.rollback(f)
             if f % 50 == 1:
                 p.check_state(with_select=False)
+
+
+def test_camera_token_stream_parity():
+    """One camera token per frame under the pool policy, its own rotary base
+    (decode-shaped: one query row per head): attention through the window's
+    filling, the first evictions and the growing trajectory of kept tokens."""
+    w = WL.CAMERA_T1
+    p = Pair(w)
+    checked = 0
+    for f in range(w.n_frames):
+        p.step(f)
+        if f < 40 or f % 10 == 0 or f == w.n_frames - 1:
+            _cmp_attention(p, f)
+            checked += 1
+    gs = p.check_state()
+    assert gs["traj_len"] == w.n_frames - w.A - w.W and checked > 130
 
 
 def test_rope_standalone_matches_oracle():
