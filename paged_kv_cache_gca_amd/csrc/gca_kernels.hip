@@ -1,11 +1,16 @@
 // HIP kernels of the GCA path for CDNA4 (gfx950, MI355X).
 //
-//   k_rope    3D (t, h, w) rotary embedding of a [T][H][D] tensor
+//   k_rope    3D (t, h, w) rotary embedding of [nf][T][H][D] (frames
+//             frame .. frame + nf - 1)
 //   k_append  pop a frame's pages, rotate K, scatter K into [page][H][P][D]
-//             and V transposed into [page][H][D][P]
+//             and V into dim-major pages (16-slot groups in operand order)
 //   k_evict   copy an evicted frame's compact tokens into trajectory pages
 //             and push the frame's pages to the ring tail
 //   k_select  gather list (page, valid tokens): anchor, window, trajectory
+//   k_prepare gather list plus the attention's prepared queries (rotated,
+//             scaled to base-2 logits, rounded once) in one launch
+//   k_update  one frame's append, eviction, query preparation and gather
+//             list in one launch (the per-frame step)
 //   k_attn    paged flash attention: K/V pages staged in LDS, S^T = K Q^T and
 //             O^T = V^T P^T on MFMA (bf16 32x32x16, or f32 32x32x2), online
 //             softmax in float32, split over the context (split-KV)
@@ -262,7 +267,8 @@ __global__ __launch_bounds__(256) void k_select(SelectArgs a) {
 }
 
 // One launch per attention call: blocks [0, sel_blocks) build the gather
-// list, the remaining blocks rotate the frame's queries into a workspace.
+// list, the remaining blocks rotate the queries (one frame's, or the scale
+// frames' together) into a workspace.
 template <typename T>
 __global__ __launch_bounds__(256) void k_prepare(SelectArgs sa, RopeArgs ra, int sel_blocks) {
   if ((int)blockIdx.x < sel_blocks) {
