@@ -411,7 +411,7 @@ def main():
         calibrate_copy()
         return
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        print(json.dumps({"error": "the GCA path runs on one GPU: --gpus must be 1"}))
         sys.exit(2)
     from paged_kv_cache_gca_amd import workloads as WL
     w = {x.name: x for x in WL.ALL}[args.workload]
