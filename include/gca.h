@@ -158,6 +158,21 @@ int gca_cache_reset(gca_cache* cache, gca_stream_t stream);
 int gca_append_frame(gca_cache* cache, int64_t frame_idx, const void* k, const void* v,
                      uint32_t flags, gca_stream_t stream);
 
+/* Several keyframes appended in one launch: append_frame for frames
+ * first_frame .. first_frame + n_frames - 1 in that order, k and v raw
+ * [n_frames][T][H][D].  Meant for the scale frames (a stream's first frames,
+ * processed together and kept as the anchor: "How the Geometric Context
+ * Transformer Enables Streaming 3D Reconstruction in LingBot-Map", section
+ * "Streaming Inference API"), or any burst of keyframes with no eviction due
+ * in between.  Results are bit for bit those of the individual calls.  The
+ * whole batch is validated first; an error leaves the cache unchanged.
+ * Errors: INVALID_ARGUMENT (null/misaligned, first_frame < 0, n_frames < 1);
+ * CAPACITY (n_frames > 16, or a frame index >= max_frames); SEQUENCE (as
+ * gca_append_frame for any frame of the batch, including an eviction coming
+ * due inside it); OUT_OF_PAGES. */
+int gca_append_frames(gca_cache* cache, int64_t first_frame, int32_t n_frames, const void* k,
+                      const void* v, gca_stream_t stream);
+
 /* evict_frames: while more than W window frames are live, take the oldest,
  * copy its C compact tokens (K' and V) to the end of the trajectory (popping a
  * new trajectory page from the ring head whenever the trajectory length is a

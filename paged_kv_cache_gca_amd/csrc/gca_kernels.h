@@ -51,6 +51,16 @@ struct AppendArgs {
   RopeTabs tabs;
 };
 
+// Several keyframes appended in one launch: frame j (0 <= j < n) reads its
+// inputs at k, v + j * T * H * D elements, pops ring positions ring_pos + j *
+// ppf onwards and fills record slot slot[j]; `a` holds frame 0's arguments.
+constexpr int kMaxAppendBatch = 16;
+struct AppendBatch {
+  AppendArgs a;
+  int n;
+  int slot[kMaxAppendBatch];
+};
+
 struct EvictArgs {
   void* kpool;
   void* vpool;
@@ -126,6 +136,7 @@ struct RopeArgs {
 
 // Launchers (defined in gca_kernels.hip).  dtype: 0 float32, 1 bfloat16.
 hipError_t launch_append(int dtype, const AppendArgs& a, hipStream_t s);
+hipError_t launch_append_batch(int dtype, const AppendBatch& b, hipStream_t s);
 hipError_t launch_evict(int dtype, const EvictArgs& a, hipStream_t s);
 hipError_t launch_select(const SelectArgs& a, hipStream_t s);
 // gather list and query rotation (into ra.y) in one launch

@@ -170,6 +170,20 @@ __global__ __launch_bounds__(256) void k_append(AppendArgs a) {
   append_block<T>(a, blockIdx.x, blockIdx.y);
 }
 
+// workgroup (j * ppf + i, h): page i of frame j of the batch, head h
+template <typename T>
+__global__ __launch_bounds__(256) void k_append_batch(AppendBatch b) {
+  const int j = blockIdx.x / b.a.ppf, i = blockIdx.x - j * b.a.ppf;
+  AppendArgs a = b.a;
+  const size_t fe = (size_t)a.T * a.H * kHeadDim;
+  a.k = (const T*)b.a.k + j * fe;
+  a.v = (const T*)b.a.v + j * fe;
+  a.ring_pos = b.a.ring_pos + (int64_t)j * a.ppf;
+  a.frame = b.a.frame + j;
+  a.slot = b.slot[j];
+  append_block<T>(a, i, blockIdx.y);
+}
+
 // ---------------------------------------------------------------------------
 // Evict one frame: workgroup h copies the C compact tokens of head h; block 0
 // also records the trajectory pages it pops and pushes the frame's pages to
@@ -1180,6 +1194,14 @@ hipError_t launch_append(int dtype, const AppendArgs& a, hipStream_t s) {
   dim3 grid(a.ppf, a.H);
   if (dtype) hipLaunchKernelGGL(k_append<bf16>, grid, dim3(256), 0, s, a);
   else hipLaunchKernelGGL(k_append<float>, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_append_batch(int dtype, const AppendBatch& b, hipStream_t s) {
+  if (b.n < 1 || b.n > kMaxAppendBatch) return hipErrorInvalidValue;
+  dim3 grid(b.a.ppf * b.n, b.a.H);
+  if (dtype) hipLaunchKernelGGL(k_append_batch<bf16>, grid, dim3(256), 0, s, b);
+  else hipLaunchKernelGGL(k_append_batch<float>, grid, dim3(256), 0, s, b);
   return hipGetLastError();
 }
 

@@ -461,6 +461,40 @@ int gca_append_frame(gca_cache* c, int64_t frame_idx, const void* k, const void*
   return GCA_OK;
 }
 
+int gca_append_frames(gca_cache* c, int64_t first_frame, int32_t n_frames, const void* k, const void* v,
+                      gca_stream_t stream) {
+  if (!c || !aligned16(k) || !aligned16(v) || first_frame < 0 || n_frames < 1)
+    return GCA_ERR_INVALID_ARGUMENT;
+  if (n_frames > gca::kMaxAppendBatch) return GCA_ERR_CAPACITY;
+  // every append on a copy of the planner first, as the individual calls
+  // would run them; nothing is enqueued or changed unless all are valid
+  gca::Planner p = c->plan;
+  gca::AppendBatch b{};
+  int64_t pos0 = 0;
+  for (int j = 0; j < n_frames; ++j) {
+    gca::AppendStep st;
+    int rc = p.check_append(first_frame + j, false, &st);
+    if (rc) return rc;
+    if (j == 0) {
+      b.a = append_args(c, st, k, v);
+      pos0 = st.ring_pos;
+    } else if (st.ring_pos != pos0 + (int64_t)j * c->g.ppf) {
+      return GCA_ERR_SEQUENCE;  // not reached: with no eviction between them the pops are consecutive
+    }
+    b.slot[j] = st.slot;
+    p.commit_append(st, false);
+  }
+  b.n = n_frames;
+  hipStream_t s = (hipStream_t)stream;
+  {
+    Prof pr(c, 0, s);
+    GCA_HIP(gca::launch_append_batch(c->g.dtype, b, s), "append kernel launch");
+  }
+  c->plan = p;
+  c->sel_valid = false;
+  return GCA_OK;
+}
+
 int gca_evict_compact(gca_cache* c, gca_stream_t stream) {
   if (!c) return GCA_ERR_INVALID_ARGUMENT;
   std::vector<gca::EvictStep> steps;

@@ -80,6 +80,7 @@ def _load():
         "gca_evict_compact": [vp, vp],
         "gca_attend": [vp, i64, vp, vp, vp, vp],
         "gca_attend_frames": [vp, i64, i32, vp, vp, vp, vp],
+        "gca_append_frames": [vp, i64, i32, vp, vp, vp],
         "gca_rollback_last_frame": [vp, i64, vp],
         "gca_step": [vp, i64, vp, vp, vp, vp, vp, u32, vp],
         "gca_select": [vp, vp],
@@ -266,6 +267,10 @@ class Cache:
 
     def attend(self, frame: int, q, out, lse=None, stream=None) -> int:
         return _lib.gca_attend(self.h, frame, _ptr(q), _ptr(out), _ptr(lse), _stream(stream))
+
+    def append_frames(self, first: int, k, v, stream=None) -> int:
+        """keyframes first .. first+n-1 in one launch: k, v [n][T][H][D]"""
+        return _lib.gca_append_frames(self.h, first, int(k.shape[0]), _ptr(k), _ptr(v), _stream(stream))
 
     def attend_frames(self, first: int, q, out, lse=None, stream=None) -> int:
         """scale frames together: q [n][T][H][D] of frames first .. first+n-1"""

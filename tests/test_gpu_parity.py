@@ -513,10 +513,17 @@ def _lib_step(c, frame, k, v, q, out, flags=1, q_offset=0):
 # --------------------------------------------------------------------------- scale frames
 
 
-def _scale_pair(T, H, P, dtype, A, rope, ns, gh, gw, seed=43, out_dtype="f32"):
+def _scale_pair(T, H, P, dtype, A, rope, ns, gh, gw, seed=43, out_dtype="f32", batch=False):
     w = WL.Workload("scale", T=T, H=H, D=64, P=P, dtype=dtype, n_frames=A + 2, A=A, W=2, C=3,
                     rope=rope, num_special=ns, grid_h=gh, grid_w=gw, seed=seed)
     p = Pair(w, out_dtype=out_dtype)
+    if batch:  # the anchor frames in one launch (the oracle appends them one by one)
+        kv = [p.fs.kv(f) for f in range(A)]
+        k, v = np.stack([x[0] for x in kv]), np.stack([x[1] for x in kv])
+        assert p.gpu.append_frames(0, dev(k, dtype), dev(v, dtype)) == 0
+        for f in range(A):
+            assert p.orc.append(f, kv[f][0], kv[f][1]) == 0 and p.orc.evict() == 0
+        return p
     for f in range(A):
         p.step(f)
     return p
@@ -532,19 +539,21 @@ def _attend_frames(p, first, nf):
     return q, out, lse
 
 
-@pytest.mark.parametrize("T,H,P,dtype,A,nf,rope,ns,gh,gw,sampled,out_dtype", [
-    (64, 2, 16, "f32", 3, 3, 0, 0, 8, 8, False, "f32"),         # fp32, every row
-    (300, 4, 16, "bf16", 4, 4, 1, 3, 9, 33, False, "f32"),      # several q tiles, ragged tail
-    (300, 4, 64, "bf16", 4, 2, 1, 3, 9, 33, False, "f32"),      # the last two of four anchors
-    (300, 12, 32, "bf16", 3, 3, 1, 3, 9, 33, False, "bf16"),    # H not a multiple of 8, bf16 out
-    (1004, 16, 16, "bf16", 8, 8, 1, 5, 27, 37, True, "f32"),    # 8 scale frames at the frame shape
-    (1004, 16, 64, "bf16", 4, 4, 1, 5, 27, 37, True, "f32"),
+@pytest.mark.parametrize("T,H,P,dtype,A,nf,rope,ns,gh,gw,sampled,out_dtype,batch", [
+    (64, 2, 16, "f32", 3, 3, 0, 0, 8, 8, False, "f32", True),       # fp32, every row
+    (300, 4, 16, "bf16", 4, 4, 1, 3, 9, 33, False, "f32", False),   # several q tiles, ragged tail
+    (300, 4, 64, "bf16", 4, 2, 1, 3, 9, 33, False, "f32", True),    # the last two of four anchors
+    (300, 12, 32, "bf16", 3, 3, 1, 3, 9, 33, False, "bf16", False), # H not a multiple of 8, bf16 out
+    (1004, 16, 16, "bf16", 8, 8, 1, 5, 27, 37, True, "f32", True),  # 8 scale frames at the frame shape
+    (1004, 16, 64, "bf16", 4, 4, 1, 5, 27, 37, True, "f32", False),
 ])
-def test_scale_frames_joint_attention_parity(T, H, P, dtype, A, nf, rope, ns, gh, gw, sampled, out_dtype):
-    """The anchors' queries in one call, each frame rotated at its own index, over the
-    context of all anchors (bidirectional), against the oracle frame by frame; then
-    the stream goes on causally over that anchor."""
-    p = _scale_pair(T, H, P, dtype, A, rope, ns, gh, gw, out_dtype=out_dtype)
+def test_scale_frames_joint_attention_parity(T, H, P, dtype, A, nf, rope, ns, gh, gw, sampled, out_dtype,
+                                             batch):
+    """The anchors (appended one by one, or in one batch) and their queries in one call,
+    each frame rotated at its own index, over the context of all anchors
+    (bidirectional), against the oracle frame by frame; then the stream goes on
+    causally over that anchor."""
+    p = _scale_pair(T, H, P, dtype, A, rope, ns, gh, gw, out_dtype=out_dtype, batch=batch)
     first = A - nf
     rows = (np.unique(np.r_[np.arange(0, T, 61), 255, 256, T - 1]).astype(np.int32) if sampled
             else np.arange(T, dtype=np.int32))
@@ -587,3 +596,54 @@ def test_scale_frames_errors_change_nothing():
     after = p.gpu.export_state()
     for key in ("free", "frame_idx", "frame_pages", "traj_pages"):
         np.testing.assert_array_equal(before[key], after[key])
+
+
+@pytest.mark.parametrize("T,H,P,dtype,A,n,rope,ns,gh,gw", [
+    (300, 4, 16, "bf16", 8, 8, 1, 3, 9, 33),
+    (1004, 16, 64, "bf16", 4, 4, 1, 5, 27, 37),
+    (64, 2, 32, "f32", 1, 3, 0, 0, 8, 8),        # anchor, then two window frames
+])
+def test_append_frames_is_the_individual_calls_bitwise(T, H, P, dtype, A, n, rope, ns, gh, gw):
+    """One batched launch equals n gca_append_frame calls bit for bit (state and every
+    live page), and matches the oracle's appends."""
+    w = WL.Workload("batch", T=T, H=H, D=64, P=P, dtype=dtype, n_frames=n + 2, A=A, W=2, C=3,
+                    rope=rope, num_special=ns, grid_h=gh, grid_w=gw, seed=46)
+    p = Pair(w)
+    g = gca()
+    one = g.Cache(p.cfg)
+    kv = [p.fs.kv(f) for f in range(n)]
+    k, v = np.stack([x[0] for x in kv]), np.stack([x[1] for x in kv])
+    assert p.gpu.append_frames(0, dev(k, dtype), dev(v, dtype)) == 0
+    for f in range(n):
+        assert one.append_frame(f, dev(kv[f][0], dtype), dev(kv[f][1], dtype)) == 0
+        assert p.orc.append(f, kv[f][0], kv[f][1]) == 0
+    gs = p.check_state()
+    p.check_pages(gs)
+    assert one.select() == 0
+    gs1 = one.export_state()
+    for key in ("free", "frame_idx", "frame_pages", "traj_pages", "sel_page", "sel_len"):
+        np.testing.assert_array_equal(gs[key], gs1[key])
+    for pg in np.concatenate([gs["frame_pages"].ravel(), gs["traj_pages"]]):
+        a, b = p.gpu.read_page(int(pg)), one.read_page(int(pg))
+        assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_append_frames_errors_change_nothing():
+    g = gca()
+    w = WL.Workload("batch_err", T=64, H=2, D=64, P=16, dtype="f32", n_frames=20, A=1, W=2, C=1,
+                    rope=0, num_special=0, grid_h=8, grid_w=8, seed=47)
+    p = Pair(w)
+    p.step(0)
+    before = p.gpu.export_state()
+    kk = torch.zeros((17, w.T, w.H, w.D), dtype=torch.float32, device="cuda")
+    # frames 1..4: frame 4 arrives with W + 1 window frames live, an eviction due
+    assert p.gpu.append_frames(1, kk[:4], kk[:4]) == g.GCA_ERR_SEQUENCE
+    assert p.gpu.append_frames(0, kk[:2], kk[:2]) == g.GCA_ERR_SEQUENCE      # frame 0 again
+    assert p.gpu.append_frames(1, kk, kk) == g.GCA_ERR_CAPACITY              # 17 frames
+    assert p.gpu.append_frames(1, kk[:0], kk[:0]) == g.GCA_ERR_INVALID_ARGUMENT
+    assert p.gpu.append_frames(19, kk[:2], kk[:2]) == g.GCA_ERR_CAPACITY     # frame 20 >= max_frames
+    after = p.gpu.export_state()
+    for key in ("free", "frame_idx", "frame_pages", "traj_pages"):
+        np.testing.assert_array_equal(before[key], after[key])
+    # the same batch that fits: frames 1..3
+    assert p.gpu.append_frames(1, kk[:3], kk[:3]) == 0
