@@ -219,10 +219,10 @@ def run_gpu(w, steps, warmup):
 
 
 def run_scale_phase(w, nf=8, reps=10, warmup=2):
-    """The stream's first phase: nf scale frames appended as the anchor, then all
-    of their queries in one joint (bidirectional) attention call.  HIP events
-    from the library around the attention launch; events on the stream around
-    each whole phase (nf appends + the joint call)."""
+    """The stream's first phase: nf scale frames appended as the anchor in one
+    launch, then all of their queries in one joint (bidirectional) attention
+    call.  HIP events from the library around the append and the attention
+    launches; events on the stream around each whole phase."""
     import torch
 
     from paged_kv_cache_gca_amd import gca
@@ -230,11 +230,9 @@ def run_scale_phase(w, nf=8, reps=10, warmup=2):
 
     dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     fs = FrameStream(w.seed, w.T, w.H, w.D, w.dtype, n_base=w.n_base)
-    K, V = [], []
-    for f in range(nf):
-        k, v = fs.kv(f)
-        K.append(torch.from_numpy(k).to(dt).cuda())
-        V.append(torch.from_numpy(v).to(dt).cuda())
+    kv = [fs.kv(f) for f in range(nf)]
+    K = torch.stack([torch.from_numpy(x[0]).to(dt) for x in kv]).cuda()
+    V = torch.stack([torch.from_numpy(x[1]).to(dt) for x in kv]).cuda()
     Q = torch.stack([torch.from_numpy(fs.q(f)).to(dt) for f in range(nf)]).cuda()
     cache = gca.Cache(gca.Config.from_workload(w, num_anchor_frames=nf))
     out = torch.empty((nf, w.T, w.H, w.D), dtype=torch.float32, device="cuda")
@@ -244,9 +242,8 @@ def run_scale_phase(w, nf=8, reps=10, warmup=2):
     def phase():
         if cache.reset(stream) != 0:
             raise RuntimeError("reset failed")
-        for f in range(nf):
-            if cache.append_frame(f, K[f], V[f], stream=stream) != 0 or cache.evict_compact(stream) != 0:
-                raise RuntimeError("scale-frame append failed")
+        if cache.append_frames(0, K, V, stream=stream) != 0:
+            raise RuntimeError("scale-frame append failed")
         if cache.attend_frames(0, Q, out, lse, stream=stream) != 0:
             raise RuntimeError("joint attention failed")
 
@@ -254,7 +251,7 @@ def run_scale_phase(w, nf=8, reps=10, warmup=2):
         phase()
     torch.cuda.synchronize()
     n_ctx = cache.query().n_ctx
-    cache.profile_enable(reps + 4, kinds=("attn",))
+    cache.profile_enable(reps + 4, kinds=("attn", "append"))
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
     for e0, e1 in ev:
         e0.record(stream)
@@ -262,6 +259,7 @@ def run_scale_phase(w, nf=8, reps=10, warmup=2):
         e1.record(stream)
     torch.cuda.synchronize()
     attn_ms, n = cache.profile_read("attn")
+    app_ms, na = cache.profile_read("append")
     cache.profile_enable(0)
     cache.close()
     assert torch.isfinite(out).all()
@@ -270,11 +268,20 @@ def run_scale_phase(w, nf=8, reps=10, warmup=2):
     us = attn_ms * 1e3 / max(n, 1)
     tflops = flop / (us * 1e-6) / 1e12
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_MFMA_TFLOPS
+    esize = 2 if w.dtype == "bf16" else 4
+    ppf = -(-w.T // w.P)
+    # per frame: read K and V, write both into its pages (zero tail included)
+    app_b = nf * (2 * w.T + 2 * ppf * w.P) * w.H * w.D * esize
+    app_us = app_ms * 1e3 / max(na, 1)
+    app_gbs = app_b / (app_us * 1e-6) / 1e9
     return {"frames": nf, "queries": nf * w.T, "n_ctx": n_ctx, "attn_us": round(us, 2),
             "attn_flop": flop, "achieved": round(tflops, 1), "peak": peak, "unit": "TFLOP/s",
-            "frac": round(tflops / peak, 4), "phase_us": round(phase_ms * 1e3, 1),
-            "timing": f"{reps} phases after {warmup} warm-up: library HIP events around the joint "
-                      "attention launch; stream events around each phase (appends + joint call)"}
+            "frac": round(tflops / peak, 4),
+            "append": {"us": round(app_us, 2), "bytes": app_b, "achieved": round(app_gbs, 1),
+                       "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(app_gbs / PEAK_HBM_GBS, 4)},
+            "phase_us": round(phase_ms * 1e3, 1),
+            "timing": f"{reps} phases after {warmup} warm-up: library HIP events around the batched "
+                      "append launch and the joint attention launch; stream events around each phase"}
 
 
 def scale_phase_cpu(w, nf=8, n_rows=8):
