@@ -175,6 +175,8 @@ def test_keep_every_token_and_window_never_full():
     (2, 3, 64, "bf16", 0, 2, 0, 1, 1, 1, 1, 2),    # one special + one patch token, no anchor, no trajectory
     (17, 1, 16, "bf16", 2, 1, 17, 1, 2, 3, 5, 1),  # ragged page, C = T, window of one frame
     (33, 5, 32, "f32", 1, 3, 4, 1, 0, 3, 11, 3),   # odd head count, TEMP frames
+    (3, 5, 16, "bf16", 1, 4, 2, 1, 2, 1, 1, 1),    # three query rows: the decode kernel
+    (4, 2, 32, "f32", 1, 2, 1, 1, 0, 2, 2, 2),     # four query rows, fp32, TEMP frames
 ])
 def test_degenerate_shapes(T, H, P, dtype, A, W, C, rope, ns, gh, gw, interval):
     """Tiny and ragged frames: one token, one head, a single partial page per
@@ -514,7 +516,7 @@ def _lib_step(c, frame, k, v, q, out, flags=1, q_offset=0):
 
 
 def _scale_pair(T, H, P, dtype, A, rope, ns, gh, gw, seed=43, out_dtype="f32", batch=False):
-    w = WL.Workload("scale", T=T, H=H, D=64, P=P, dtype=dtype, n_frames=A + 2, A=A, W=2, C=3,
+    w = WL.Workload("scale", T=T, H=H, D=64, P=P, dtype=dtype, n_frames=A + 2, A=A, W=2, C=min(3, T),
                     rope=rope, num_special=ns, grid_h=gh, grid_w=gw, seed=seed)
     p = Pair(w, out_dtype=out_dtype)
     if batch:  # the anchor frames in one launch (the oracle appends them one by one)
@@ -544,6 +546,7 @@ def _attend_frames(p, first, nf):
     (300, 4, 16, "bf16", 4, 4, 1, 3, 9, 33, False, "f32", False),   # several q tiles, ragged tail
     (300, 4, 64, "bf16", 4, 2, 1, 3, 9, 33, False, "f32", True),    # the last two of four anchors
     (300, 12, 32, "bf16", 3, 3, 1, 3, 9, 33, False, "bf16", False), # H not a multiple of 8, bf16 out
+    (2, 3, 16, "bf16", 2, 2, 1, 1, 1, 1, False, "f32", True),        # 2 x 2 query rows: decode kernel
     (1004, 16, 16, "bf16", 8, 8, 1, 5, 27, 37, True, "f32", True),  # 8 scale frames at the frame shape
     (1004, 16, 64, "bf16", 4, 4, 1, 5, 27, 37, True, "f32", False),
 ])
