@@ -43,6 +43,10 @@ def query_rounding_bound(pair, f, q, rows):
 
 def _cmp_attention(pair, f, rows=None):
     q, out, lse = pair.attend_gpu(f)
+    return _cmp_outputs(pair, f, q, out, lse, rows)
+
+
+def _cmp_outputs(pair, f, q, out, lse, rows=None):
     T = pair.w.T
     rows = np.arange(T, dtype=np.int32) if rows is None else np.asarray(rows, dtype=np.int32)
     o_ref, lse_ref = pair.orc.attend(f, q, rows=rows)
@@ -210,6 +214,26 @@ def test_frame1004_w16_p16_stream_sampled():
         p.check_state()
         if f in (0, 1, 16, 17, 40, 63):
             _cmp_attention(p, f, rows)
+
+
+def test_frame1004_stream_through_gca_step_sampled():
+    """The bench's own launch sequence: gca_step per frame over the 64-frame
+    1004-token stream (one update launch, the attention, the merge), its outputs
+    on sampled rows against the oracle as the window fills, at the first
+    evictions and at the end."""
+    w = WL.FRAME1004_W16
+    p = Pair(w)
+    rows = _rows(w.T, seed=3)
+    for f in range(w.n_frames):
+        k, v, kd, vd = p.kv(f)
+        q = p.fs.q(f)
+        out = torch.empty((w.T, w.H, w.D), dtype=torch.float32, device="cuda")
+        lse = torch.empty((w.T, w.H), dtype=torch.float32, device="cuda")
+        assert p.gpu.step(f, kd, vd, dev(q, w.dtype), out, lse, keyframe=True) == 0
+        assert p.orc.append(f, k, v) == 0 and p.orc.evict() == 0
+        if f in (0, 15, 16, 17, 41, 63):
+            _cmp_outputs(p, f, q, out, lse, rows)
+    p.check_state()
 
 
 @pytest.mark.parametrize("w,last,samples", [
