@@ -147,3 +147,25 @@ def test_plan_occupancy_matches_oracle_every_step(w):
             assert info.traj_tokens == st["traj_len"]
         if not key:
             assert p.rollback(f) == 0 and o.rollback(f) == 0
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py runs on one GPU: --gpus 2 exits with a message, before touching a device."""
+    import json
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in json.loads(r.stdout.strip().splitlines()[-1])["error"]
+
+
+def test_committed_counter_summary_fields():
+    """profiles/attn_traffic.json carries what the bench line reads from it."""
+    import json
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    d = json.load(open(os.path.join(root, "profiles", "attn_traffic.json")))
+    for key in ("kernel_hash", "mfma_busy", "bytes_per_launch", "fetch_scale", "write_scale"):
+        assert key in d
+    assert 0 < d["mfma_busy"] < 1 and d["bytes_per_launch"] > 0 and len(d["kernel_hash"]) == 16
