@@ -49,17 +49,24 @@ __device__ inline bf16 from_f<bf16>(float x) { return (bf16)x; }  // round to ne
 // frame index, [nt, nt+nh) the patch row, the rest the patch column; special
 // tokens sit at row 0, column 0.
 
-__device__ inline float2 rope_cs(const RopeTabs& R, int64_t frame, int tok, int pair) {
-  if (pair < R.nt) return R.t[frame * R.nt + pair];
-  int row = 0, col = 0;
-  if (tok >= R.num_special) {
-    int p = tok - R.num_special;
-    row = p / R.grid_w;
-    col = p - row * R.grid_w;
+// cos/sin of pairs `pair` and `pair` + 1 (pair even) in one 16-byte load: the
+// axis blocks have an even number of pairs (12, 10, 10 for D = 64), so both
+// lie next to each other in one table, at a 16-byte aligned offset.
+__device__ inline float4 rope_cs2(const RopeTabs& R, int64_t frame, int tok, int pair) {
+  const float2* p;
+  if (pair < R.nt) {
+    p = R.t + frame * R.nt + pair;
+  } else {
+    int row = 0, col = 0;
+    if (tok >= R.num_special) {
+      int q = tok - R.num_special;
+      row = q / R.grid_w;
+      col = q - row * R.grid_w;
+    }
+    pair -= R.nt;
+    p = pair < R.nh ? R.h + row * R.nh + pair : R.w + col * R.nw + (pair - R.nh);
   }
-  pair -= R.nt;
-  if (pair < R.nh) return R.h[row * R.nh + pair];
-  return R.w[col * R.nw + (pair - R.nh)];
+  return *(const float4*)p;
 }
 
 // One fixed operation sequence, so every kernel that rotates gives the same bits.
@@ -76,12 +83,16 @@ __device__ inline void rotate_chunk(Vec16<T>& v, const RopeTabs& R, int64_t fram
                                     int first_pair, float scale = 1.f) {
   constexpr int EPC = 16 / sizeof(T);
 #pragma unroll
-  for (int m = 0; m < EPC / 2; ++m) {
-    float2 cs = rope_cs(R, frame, tok, first_pair + m);
-    float y0, y1;
-    rotate(to_f(v.e[2 * m]), to_f(v.e[2 * m + 1]), cs, y0, y1);
-    v.e[2 * m] = from_f<T>(y0 * scale);
-    v.e[2 * m + 1] = from_f<T>(y1 * scale);
+  for (int m = 0; m < EPC / 2; m += 2) {
+    const float4 c4 = rope_cs2(R, frame, tok, first_pair + m);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const float2 cs = u ? make_float2(c4.z, c4.w) : make_float2(c4.x, c4.y);
+      float y0, y1;
+      rotate(to_f(v.e[2 * (m + u)]), to_f(v.e[2 * (m + u) + 1]), cs, y0, y1);
+      v.e[2 * (m + u)] = from_f<T>(y0 * scale);
+      v.e[2 * (m + u) + 1] = from_f<T>(y1 * scale);
+    }
   }
 }
 

@@ -401,6 +401,8 @@ int gca_cache_create(const gca_config* cfg, gca_cache** out) {
     std::vector<float2> t, h, w;
     int nt, nh, nw;
     build_rope(g, &t, &h, &w, &nt, &nh, &nw);
+    // the kernels load the cos/sin of two pairs at once (12, 10, 10 pairs for D = 64)
+    if ((nt | nh | nw) & 1) return fail(hipErrorInvalidValue, "rotary split with an odd pair count");
     if ((e = dmalloc(&c->rope_t, sizeof(float2) * t.size())) != hipSuccess) return fail(e, "hipMalloc rope");
     if ((e = dmalloc(&c->rope_h, sizeof(float2) * h.size())) != hipSuccess) return fail(e, "hipMalloc rope");
     if ((e = dmalloc(&c->rope_w, sizeof(float2) * w.size())) != hipSuccess) return fail(e, "hipMalloc rope");
