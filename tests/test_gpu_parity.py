@@ -674,3 +674,32 @@ def test_append_frames_errors_change_nothing():
         np.testing.assert_array_equal(before[key], after[key])
     # the same batch that fits: frames 1..3
     assert p.gpu.append_frames(1, kk[:3], kk[:3]) == 0
+
+
+def test_usage_flow_scale_frames_then_gca_step():
+    """The documented flow at the frame shape: 8 scale frames in one batched append,
+    their joint attention, then gca_step per frame; sampled rows against the oracle."""
+    A = 8
+    w = WL.Workload("usage", T=1004, H=16, D=64, P=16, dtype="bf16", n_frames=A + 4, A=A, W=3, C=13,
+                    rope=1, num_special=5, grid_h=27, grid_w=37, seed=48)
+    p = Pair(w)
+    rows = _rows(w.T, n=24, seed=5)
+    kv = [p.fs.kv(f) for f in range(A)]
+    k, v = np.stack([x[0] for x in kv]), np.stack([x[1] for x in kv])
+    assert p.gpu.append_frames(0, dev(k, "bf16"), dev(v, "bf16")) == 0
+    for f in range(A):
+        assert p.orc.append(f, kv[f][0], kv[f][1]) == 0 and p.orc.evict() == 0
+    q, out, lse = _attend_frames(p, 0, A)
+    o_ref, _ = p.orc.attend_frames(0, q, rows=rows)
+    for i in (0, A - 1):
+        err = float(np.abs(out[i].cpu().numpy()[rows].astype(np.float64) - o_ref[i]).max())
+        assert err <= TOL["bf16"], (i, err)
+    for f in range(A, w.n_frames):
+        k1, v1, kd, vd = p.kv(f)
+        q1 = p.fs.q(f)
+        o1 = torch.empty((w.T, w.H, w.D), dtype=torch.float32, device="cuda")
+        l1 = torch.empty((w.T, w.H), dtype=torch.float32, device="cuda")
+        assert p.gpu.step(f, kd, vd, dev(q1, "bf16"), o1, l1, keyframe=True) == 0
+        assert p.orc.append(f, k1, v1) == 0 and p.orc.evict() == 0
+        _cmp_outputs(p, f, q1, o1, l1, rows)
+    p.check_state()
