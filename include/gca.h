@@ -274,6 +274,11 @@ int gca_plan_evict(gca_plan* plan);
 int gca_plan_attend(gca_plan* plan, int64_t frame_idx);
 int gca_plan_rollback(gca_plan* plan, int64_t frame_idx);
 int gca_plan_query(const gca_plan* plan, gca_info* out);
+/* The compact token offsets the config resolves to (the given list, or the
+ * default rule: special tokens first, then evenly spaced patch tokens),
+ * copied to out[0 .. *n).  *n is always set; GCA_ERR_CAPACITY (nothing
+ * copied) when cap < *n. */
+int gca_plan_compact(const gca_plan* plan, int32_t* out, int32_t cap, int32_t* n);
 
 /* ---- diagnostics -------------------------------------------------------------- */
 const char* gca_status_string(int status);

@@ -12,7 +12,7 @@ def build(verbose: bool = False) -> str:
     out = os.path.join(_HERE, "libgca_oracle.so")
     tmp = out + ".tmp"
     # x86-64-v3 (AVX2) so the library also runs on the GPU hosts' CPUs
-    cmd = ["g++", "-std=c++17", "-O2", "-march=x86-64-v3", "-fno-fast-math", "-ffp-contract=off",
+    cmd = ["g++", "-std=c++17", "-O3", "-march=x86-64-v3", "-fno-fast-math", "-ffp-contract=off",
            "-fPIC", "-shared", "-pthread", src, "-o", tmp]
     if verbose:
         print(" ".join(cmd))

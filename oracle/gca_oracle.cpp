@@ -50,6 +50,7 @@
 //    nearest even, or float32); attention itself is evaluated in float64.
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -494,41 +495,49 @@ static void attend_over(const Cfg& c, const std::vector<float>& K, const std::ve
                         long long n, const std::vector<float>& Qp, const int32_t* rows,
                         int32_t n_rows, double* out, double* lse, int32_t threads) {
   size_t hd = (size_t)c.H * c.D;
-  auto work = [&](int h0, int h1) {
-    std::vector<double> sc(n);
-    for (int hh = h0; hh < h1; ++hh)
-      for (int ri = 0; ri < n_rows; ++ri) {
-        int t = rows[ri];
-        const float* qv = Qp.data() + ((size_t)t * c.H + hh) * c.D;
-        double m = -INFINITY;
-        for (long long j = 0; j < n; ++j) {
-          const float* kv = K.data() + (size_t)j * hd + (size_t)hh * c.D;
-          double dot = 0.0;
-          for (int d = 0; d < c.D; ++d) dot += (double)qv[d] * (double)kv[d];
-          sc[j] = c.scale * dot;
-          m = std::max(m, sc[j]);
-        }
-        double l = 0.0;
-        for (long long j = 0; j < n; ++j) {
-          sc[j] = std::exp(sc[j] - m);
-          l += sc[j];
-        }
-        double* o = out + ((size_t)ri * c.H + hh) * c.D;
-        for (int d = 0; d < c.D; ++d) o[d] = 0.0;
-        for (long long j = 0; j < n; ++j) {
-          const float* vv = V.data() + (size_t)j * hd + (size_t)hh * c.D;
-          for (int d = 0; d < c.D; ++d) o[d] += sc[j] * (double)vv[d];
-        }
-        for (int d = 0; d < c.D; ++d) o[d] /= l;
-        if (lse) lse[(size_t)ri * c.H + hh] = m + std::log(l);
-      }
+  // one (row, head): two passes over the context (max, then exponentials,
+  // row sum and the weighted sum of V)
+  auto one = [&](int ri, int hh, std::vector<double>& sc) {
+    int t = rows[ri];
+    const float* qv = Qp.data() + ((size_t)t * c.H + hh) * c.D;
+    double m = -INFINITY;
+    for (long long j = 0; j < n; ++j) {
+      const float* kv = K.data() + (size_t)j * hd + (size_t)hh * c.D;
+      double dot = 0.0;
+      for (int d = 0; d < c.D; ++d) dot += (double)qv[d] * (double)kv[d];
+      sc[j] = c.scale * dot;
+      m = std::max(m, sc[j]);
+    }
+    double l = 0.0;
+    for (long long j = 0; j < n; ++j) {
+      sc[j] = std::exp(sc[j] - m);
+      l += sc[j];
+    }
+    double* o = out + ((size_t)ri * c.H + hh) * c.D;
+    for (int d = 0; d < c.D; ++d) o[d] = 0.0;
+    for (long long j = 0; j < n; ++j) {
+      const float* vv = V.data() + (size_t)j * hd + (size_t)hh * c.D;
+      for (int d = 0; d < c.D; ++d) o[d] += sc[j] * (double)vv[d];
+    }
+    for (int d = 0; d < c.D; ++d) o[d] /= l;
+    if (lse) lse[(size_t)ri * c.H + hh] = m + std::log(l);
   };
-  int nt = std::max(1, std::min<int>(threads > 0 ? threads : 1, c.H));
+  // work units (head, block of 64 rows), taken in turn by the threads; each
+  // (row, head) is computed the same way whatever the thread count
+  const int RB = 64;
+  const int nrb = (n_rows + RB - 1) / RB;
+  const int units = c.H * nrb;
+  std::atomic<int> next{0};
+  auto work = [&]() {
+    std::vector<double> sc(n);
+    for (int u = next++; u < units; u = next++) {
+      int hh = u / nrb, r0 = (u % nrb) * RB, r1 = std::min<int>(n_rows, r0 + RB);
+      for (int ri = r0; ri < r1; ++ri) one(ri, hh, sc);
+    }
+  };
+  int nt = std::max(1, std::min<int>(threads > 0 ? threads : 1, units));
   std::vector<std::thread> pool;
-  for (int i = 0; i < nt; ++i) {
-    int h0 = c.H * i / nt, h1 = c.H * (i + 1) / nt;
-    pool.emplace_back(work, h0, h1);
-  }
+  for (int i = 0; i < nt; ++i) pool.emplace_back(work);
   for (auto& th : pool) th.join();
 }
 

@@ -296,6 +296,15 @@ int gca_plan_query(const gca_plan* plan, gca_info* out) {
   return GCA_OK;
 }
 
+int gca_plan_compact(const gca_plan* plan, int32_t* out, int32_t cap, int32_t* n) {
+  if (!plan || !n || cap < 0 || (cap > 0 && !out)) return GCA_ERR_INVALID_ARGUMENT;
+  const std::vector<int>& c = plan->p.geometry().compact;
+  *n = (int32_t)c.size();
+  if ((int32_t)c.size() > cap) return GCA_ERR_CAPACITY;
+  for (size_t j = 0; j < c.size(); ++j) out[j] = c[j];
+  return GCA_OK;
+}
+
 const char* gca_status_string(int s) {
   switch (s) {
     case GCA_OK: return "ok";

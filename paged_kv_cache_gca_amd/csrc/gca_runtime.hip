@@ -10,7 +10,6 @@
 #include <cstdio>
 #include <cstring>
 #include <string>
-#include <cstdlib>
 #include <vector>
 
 #include "../../include/gca.h"
@@ -352,10 +351,6 @@ int gca_cache_create(const gca_config* cfg, gca_cache** out) {
   // first's at P = 16 (register-staged tiles) and 1.84x at P = 64 (tiles
   // loaded straight into LDS), and the first one speeds up once it runs alone
   c->split_ratio = g.P >= 64 ? 1.9f : 1.7f;
-  if (const char* r = std::getenv("GCA_SPLIT_RATIO")) {  // tuning: split size ratio, <= 1 disables
-    float v = std::strtof(r, nullptr);
-    if (v > 0.f && v < 16.f) c->split_ratio = v;
-  }
   size_t page_elems = (size_t)g.H * g.P * g.D;
   // pages [0, N) are handed out by the ring; page N stays zero forever and
   // pads the gather list

@@ -98,6 +98,7 @@ def _load():
         "gca_plan_attend": [vp, i64],
         "gca_plan_rollback": [vp, i64],
         "gca_plan_query": [vp, C.POINTER(gca_info)],
+        "gca_plan_compact": [vp, C.POINTER(i32), i32, C.POINTER(i32)],
     }
     for name, args in sigs.items():
         f = getattr(L, name)
@@ -197,6 +198,36 @@ def _ptr(t):
     return C.c_void_p(t.data_ptr()) if t is not None else None
 
 
+def check_tensors(specs, device: int | None = None):
+    """Refuse tensors the kernels would read or write out of bounds.  `specs`
+    lists (tensor, name, dtype, numel): each must be a torch tensor of `dtype`
+    ("bf16" | "f32"), contiguous, with `numel` elements; then every one must be
+    on the GPU (device index `device` when given).  Raises GCAError
+    (GCA_ERR_INVALID_ARGUMENT) before anything reaches the library."""
+    import torch
+    for t, what, dtype, numel in specs:
+        want = {"bf16": torch.bfloat16, "f32": torch.float32}[dtype]
+        why = None
+        if not isinstance(t, torch.Tensor):
+            why = f"not a torch tensor ({type(t).__name__})"
+        elif t.dtype != want:
+            why = f"dtype {t.dtype}, expected {want}"
+        elif not t.is_contiguous():
+            why = "not contiguous"
+        elif t.numel() != numel:
+            why = f"{t.numel()} elements, expected {numel}"
+        if why is not None:
+            raise GCAError(GCA_ERR_INVALID_ARGUMENT, f"{what}: {why}")
+    for t, what, _, _ in specs:
+        why = None
+        if t.device.type != "cuda":
+            why = f"on {t.device}, expected a GPU tensor"
+        elif device is not None and t.device.index != device:
+            why = f"on {t.device}, the cache lives on cuda:{device}"
+        if why is not None:
+            raise GCAError(GCA_ERR_INVALID_ARGUMENT, f"{what}: {why}")
+
+
 class Plan:
     """Host-only occupancy planner (no device)."""
 
@@ -231,6 +262,14 @@ class Plan:
         _check(_lib.gca_plan_query(self.h, C.byref(inf)), "gca_plan_query")
         return inf
 
+    def compact(self) -> list[int]:
+        """The compact token offsets the config resolves to."""
+        n = C.c_int32()
+        _lib.gca_plan_compact(self.h, None, 0, C.byref(n))
+        buf = (C.c_int32 * max(n.value, 1))()
+        _check(_lib.gca_plan_compact(self.h, buf, n.value, C.byref(n)), "gca_plan_compact")
+        return list(buf[:n.value])
+
 
 class Cache:
     """A GCA paged KV cache on the current HIP device."""
@@ -242,6 +281,8 @@ class Cache:
         _check(_lib.gca_cache_create(C.byref(c), C.byref(h)), "gca_cache_create")
         self.h = h
         self.info = self.query()
+        import torch
+        self.device = torch.cuda.current_device()
 
     def close(self):
         if getattr(self, "h", None):
@@ -258,7 +299,20 @@ class Cache:
     def reset(self, stream=None) -> int:
         return _lib.gca_cache_reset(self.h, _stream(stream))
 
+    # shapes the kernels read and write: one frame is [T][H][D] of the cache
+    # dtype (queries, keys, values) or of out_dtype (outputs); lse is [T][H] f32
+    def _validate(self, n: int = 1, out=None, lse=None, **inputs):
+        c = self.cfg
+        rows = n * c.tokens_per_frame * c.num_heads
+        specs = [(t, name, c.dtype, rows * c.head_dim) for name, t in inputs.items()]
+        if out is not None:
+            specs.append((out, "out", c.out_dtype, rows * c.head_dim))
+        if lse is not None:
+            specs.append((lse, "lse", "f32", rows))
+        check_tensors(specs, self.device)
+
     def append_frame(self, frame: int, k, v, temp: bool = False, stream=None) -> int:
+        self._validate(k=k, v=v)
         return _lib.gca_append_frame(self.h, frame, _ptr(k), _ptr(v),
                                      GCA_APPEND_TEMP if temp else 0, _stream(stream))
 
@@ -266,14 +320,23 @@ class Cache:
         return _lib.gca_evict_compact(self.h, _stream(stream))
 
     def attend(self, frame: int, q, out, lse=None, stream=None) -> int:
+        self._validate(out=out, lse=lse, q=q)
         return _lib.gca_attend(self.h, frame, _ptr(q), _ptr(out), _ptr(lse), _stream(stream))
 
     def append_frames(self, first: int, k, v, stream=None) -> int:
         """keyframes first .. first+n-1 in one launch: k, v [n][T][H][D]"""
+        n = int(k.shape[0]) if hasattr(k, "shape") and len(k.shape) else 0
+        if n < 1 or not hasattr(v, "shape") or int(v.shape[0]) != n:
+            raise GCAError(GCA_ERR_INVALID_ARGUMENT, "append_frames: k and v need the same leading frame count")
+        self._validate(n, k=k, v=v)
         return _lib.gca_append_frames(self.h, first, int(k.shape[0]), _ptr(k), _ptr(v), _stream(stream))
 
     def attend_frames(self, first: int, q, out, lse=None, stream=None) -> int:
         """scale frames together: q [n][T][H][D] of frames first .. first+n-1"""
+        n = int(q.shape[0]) if hasattr(q, "shape") and len(q.shape) else 0
+        if n < 1:
+            raise GCAError(GCA_ERR_INVALID_ARGUMENT, "attend_frames: q needs a leading frame count")
+        self._validate(n, out=out, lse=lse, q=q)
         return _lib.gca_attend_frames(self.h, first, int(q.shape[0]), _ptr(q), _ptr(out), _ptr(lse),
                                       _stream(stream))
 
@@ -282,6 +345,7 @@ class Cache:
 
     def step(self, frame: int, k, v, q, out, lse=None, keyframe: bool = True, stream=None) -> int:
         """append (+ evict) + attend (+ rollback for a non-keyframe) in one call"""
+        self._validate(out=out, lse=lse, k=k, v=v, q=q)
         return _lib.gca_step(self.h, frame, _ptr(k), _ptr(v), _ptr(q), _ptr(out), _ptr(lse),
                              STEP_KEYFRAME if keyframe else 0, _stream(stream))
 
@@ -289,6 +353,7 @@ class Cache:
         return _lib.gca_select(self.h, _stream(stream))
 
     def rope3d(self, frame: int, x, y, stream=None) -> int:
+        self._validate(x=x, y=y)
         return _lib.gca_rope3d(self.h, frame, _ptr(x), _ptr(y), _stream(stream))
 
     def query(self) -> gca_info:

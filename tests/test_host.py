@@ -113,6 +113,23 @@ def test_plan_out_of_pages_changes_nothing():
         assert getattr(before, f) == getattr(after, f)
 
 
+@pytest.mark.parametrize("w,expected", [
+    (WL.TINY_F32, [0]),
+    (WL.FRAME1004_W16, [0, 1, 2, 3, 4, 5, 129, 254, 379, 504, 629, 754, 879]),
+    (WL.STREAM1000_W64, [0, 1, 2, 3, 4, 5, 129, 254, 379, 504, 629, 754, 879]),
+    (WL.STREAM10K_KF4, [0, 1, 2, 3, 4, 5, 129, 254, 379, 504, 629, 754, 879]),
+    (WL.RING20K_W12, []),
+    (WL.CAMERA_T1, [0]),
+], ids=lambda x: getattr(x, "name", ""))
+def test_library_compact_offsets_pinned(w, expected):
+    """The library's default compact list, read from its planner: the
+    hand-derived lists of the compact-token reading (special tokens first,
+    then evenly spaced patches), and a given list is kept as given."""
+    from paged_kv_cache_gca_amd import gca
+    assert gca.Plan(cfg_of(w)).compact() == expected
+    assert gca.Plan(cfg_of(WL.TINY_F32, num_compact=3, compact_idx=[7, 2, 63])).compact() == [7, 2, 63]
+
+
 def test_default_num_pages_matches_oracle_rule():
     from paged_kv_cache_gca_amd import gca
     for w in WL.ALL:
@@ -169,3 +186,49 @@ def test_committed_counter_summary_fields():
     for key in ("kernel_hash", "mfma_busy", "bytes_per_launch", "fetch_scale", "write_scale"):
         assert key in d
     assert 0 < d["mfma_busy"] < 1 and d["bytes_per_launch"] > 0 and len(d["kernel_hash"]) == 16
+
+
+def test_binding_refuses_bad_tensors_before_the_library():
+    """Tensors the kernels would read or write out of bounds never reach the C
+    ABI: wrong dtype, strided, short, or not on the GPU (checked in that order,
+    so every rule shows on the CPU).  The cache handle is null here, so a
+    tensor that got through would come back as GCA_ERR_INVALID_ARGUMENT from
+    the library instead of raising."""
+    import torch
+    from paged_kv_cache_gca_amd import gca
+    w = WL.TINY_F32
+    c = object.__new__(gca.Cache)
+    c.cfg = cfg_of(w)
+    c.h = None
+    c.device = 0
+    shape = (w.T, w.H, w.D)
+    good = torch.zeros(shape, dtype=torch.float32)
+    bad = {
+        "dtype": torch.zeros(shape, dtype=torch.bfloat16),
+        "contiguous": torch.zeros((w.H, w.T, w.D), dtype=torch.float32).transpose(0, 1),
+        "elements": torch.zeros((w.T - 1, w.H, w.D), dtype=torch.float32),
+        "GPU": good,
+    }
+    calls = [
+        lambda t: c.append_frame(0, t, good),
+        lambda t: c.append_frame(0, good, t),
+        lambda t: c.attend(0, t, good),
+        lambda t: c.attend(0, good, t),
+        lambda t: c.step(0, good, good, good, t),
+        lambda t: c.rope3d(0, t, good),
+        lambda t: c.append_frames(0, t[None], good[None]),
+        lambda t: c.attend_frames(0, t[None], good[None]),
+    ]
+    for rule, t in bad.items():
+        for call in calls:
+            with pytest.raises(gca.GCAError) as ei:
+                call(t)
+            assert ei.value.code == gca.GCA_ERR_INVALID_ARGUMENT
+            assert rule in str(ei.value) or rule == "elements" and "elements" in str(ei.value)
+    # lse: float32 [T][H]
+    with pytest.raises(gca.GCAError):
+        c.attend(0, good, good, torch.zeros((w.T, w.H), dtype=torch.float64))
+    # frame counts of the batched calls must agree
+    with pytest.raises(gca.GCAError):
+        c.append_frames(0, torch.stack([good, good]), good[None])
+    c.h = None

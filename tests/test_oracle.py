@@ -359,6 +359,65 @@ def test_rope_composition_and_axes():
         assert w[0] == pytest.approx(1.0) and 1e-4 < w[-1] < 1.0
 
 
+def test_rope_pair_frequencies_closed_form():
+    """Reading R8 of the 3D rotary embedding ("How the Geometric Context
+    Transformer...", section "3D Rotary Positional Embeddings": a (t, h, w)
+    rotary embedding over the global frame index and the patch grid): pair j
+    of an axis block of width d turns by pos * theta^(-2j/d).  For D = 64 the
+    blocks are t: d = 24 (12 pairs), h and w: d = 20 (10 pairs each); with
+    theta = 10^4 that is 10^(-j/3) per frame in the t block and 10^(-2j/5) per
+    row or column in the h and w blocks.  The last pairs turn at
+    10^(-11/3) = 2.1544346900318845e-4 and 10^(-18/5) = 2.5118864315095795e-4
+    (a theta^(-j/d) slip would give 1.47e-2)."""
+    cfg1 = _rcfg(T=1004, H=1)
+    last_t, last_hw = 2.1544346900318845e-4, 2.5118864315095795e-4
+    # one frame, special token 0 (row 0, column 0): only the t block turns
+    for j in range(12):
+        assert oracle.rope_angle(cfg1, 1, 0, j) == pytest.approx(10.0 ** (-j / 3.0), rel=1e-13)
+    for j in range(12, 32):
+        assert oracle.rope_angle(cfg1, 1, 0, j) == 0.0
+    assert oracle.rope_angle(cfg1, 1, 0, 11) == pytest.approx(last_t, rel=1e-13)
+    # frame 0, patch at row 1, column 0 (token 5 + 37): only the h block turns
+    tok_r1 = 5 + 37
+    for j in range(10):
+        assert oracle.rope_angle(cfg1, 0, tok_r1, 12 + j) == pytest.approx(10.0 ** (-2 * j / 5.0), rel=1e-13)
+        assert oracle.rope_angle(cfg1, 0, tok_r1, 22 + j) == 0.0
+    assert oracle.rope_angle(cfg1, 0, tok_r1, 21) == pytest.approx(last_hw, rel=1e-13)
+    # frame 0, patch at row 0, column 1 (token 6): only the w block turns
+    for j in range(10):
+        assert oracle.rope_angle(cfg1, 0, 6, 12 + j) == 0.0
+        assert oracle.rope_angle(cfg1, 0, 6, 22 + j) == pytest.approx(10.0 ** (-2 * j / 5.0), rel=1e-13)
+    assert oracle.rope_angle(cfg1, 0, 6, 31) == pytest.approx(last_hw, rel=1e-13)
+    # angles grow linearly in the position: frame 7, row 26, column 36 (the last patch)
+    assert oracle.rope_angle(cfg1, 7, 1003, 11) == pytest.approx(7 * last_t, rel=1e-13)
+    assert oracle.rope_angle(cfg1, 7, 1003, 21) == pytest.approx(26 * last_hw, rel=1e-13)
+    assert oracle.rope_angle(cfg1, 7, 1003, 31) == pytest.approx(36 * last_hw, rel=1e-13)
+
+
+# Compact tokens: the pages say only that an evicted frame keeps a few compact
+# tokens ("LingBot-Map runs 10,000 frames...", section "How GCT's
+# Anchor-Pose-Trajectory Pools Make Monocular 3D Tractable").  Reading R3's
+# default: the S special tokens first (offsets 0 .. min(C, S) - 1), then the
+# C - S patch offsets S + floor(j * (T - S) / (C - S)), j = 0 .. C - S - 1.
+# Worked by hand: T = 1004, S = 5, C = 13 -> 8 patches over 999:
+# floor(999 j / 8) = 0, 124, 249, 374, 499, 624, 749, 874, plus 5.
+COMPACT_CASES = [
+    ((1004, 5, 13), [0, 1, 2, 3, 4, 5, 129, 254, 379, 504, 629, 754, 879]),
+    ((64, 0, 1), [0]),
+    ((1, 0, 1), [0]),
+    ((64, 0, 4), [0, 16, 32, 48]),
+    ((300, 3, 5), [0, 1, 2, 3, 151]),     # 2 patches over 297: floor(297/2) = 148
+    ((1004, 5, 3), [0, 1, 2]),            # fewer kept tokens than special tokens
+    ((1004, 5, 5), [0, 1, 2, 3, 4]),
+]
+
+
+@pytest.mark.parametrize("shape,expected", COMPACT_CASES)
+def test_default_compact_offsets_pinned(shape, expected):
+    T, S, C_ = shape
+    assert oracle.default_compact(T, S, C_) == expected
+
+
 # --------------------------------------------------------------------------- attention
 
 
