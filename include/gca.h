@@ -227,6 +227,29 @@ enum { GCA_STEP_KEYFRAME = 1u };
 int gca_step(gca_cache* cache, int64_t frame_idx, const void* k, const void* v, const void* q,
              void* out, float* lse, uint32_t flags, gca_stream_t stream);
 
+/* gca_step for callers that cannot allocate device memory while they run:
+ * code under HIP graph capture, serving loops and harnesses that forbid
+ * hipMalloc.  Same arguments, validation, errors and results as gca_step
+ * (bit for bit), and it calls no allocating routine: the step's scratch (the
+ * prepared queries, then the split-KV partials of the attention) comes from a
+ * fixed library-wide device array of GCA_STATIC_SCRATCH_BYTES instead of the
+ * cache's workspace.  The cache itself is allocated once, by
+ * gca_cache_create, which also looks the array up on its device.
+ * Limit: the step needs T*H*64*esize bytes of queries plus, when the context
+ * is split S ways (about two workgroups per compute unit), S*T*H*65*4 bytes of
+ * partials, each rounded up to 256 bytes (about 36 MB for 1004 tokens x 16
+ * heads at S = 8); a step needing more returns GCA_ERR_CAPACITY, enqueues
+ * nothing and changes nothing (gca_last_error says how much it needed).
+ * Sharing: each GPU holds one copy of the array, from the first cache created
+ * on it until the process ends, shared by every cache and stream on that GPU
+ * and keeping the last call's contents (every byte a step reads it has
+ * written first, so nothing needs clearing).  Calls that may overlap on one
+ * GPU (other streams, other threads) race on it: order them, or use
+ * gca_step. */
+#define GCA_STATIC_SCRATCH_BYTES (64u << 20)
+int gca_step_static(gca_cache* cache, int64_t frame_idx, const void* k, const void* v, const void* q,
+                    void* out, float* lse, uint32_t flags, gca_stream_t stream);
+
 /* ---- pieces of the path, for tests and tools ------------------------------- */
 
 /* Build the gather list of the current context on the device (gca_attend does
@@ -282,7 +305,8 @@ int gca_plan_compact(const gca_plan* plan, int32_t* out, int32_t cap, int32_t* n
 
 /* ---- diagnostics -------------------------------------------------------------- */
 const char* gca_status_string(int status);
-const char* gca_last_error(void); /* text of the last GCA_ERR_HIP on this thread */
+const char* gca_last_error(void); /* text of the last GCA_ERR_HIP (or gca_step_static's
+                                     GCA_ERR_CAPACITY) on this thread */
 
 #ifdef __cplusplus
 }

@@ -9,6 +9,7 @@
 #include <cmath>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -36,6 +37,43 @@ int hip_fail(hipError_t e, const char* what) {
 bool aligned16(const void* p) { return p && ((uintptr_t)p & 15) == 0; }
 
 constexpr int kMaxSplits = 16;
+
+// Per-call scratch of gca_step_static (prepared queries, split partials): a
+// fixed array in device memory, one copy per GPU the library runs on, held
+// until the process ends.  Host code never uses the name `scratch` as an
+// address: each device's copy is looked up once (hipGetSymbolAddress, with
+// that device current) and passed to the kernels as a plain pointer.
+constexpr size_t kStaticScratchBytes = (size_t)GCA_STATIC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+std::mutex g_scratch_mu;
+std::vector<void*> g_scratch_ptr;  // by device index; null until looked up
+
+// This device's copy of `scratch` (the device must be current).
+hipError_t static_scratch(int device, void** out) {
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (device < 0) return hipErrorInvalidDevice;
+  if ((size_t)device >= g_scratch_ptr.size()) g_scratch_ptr.resize(device + 1, nullptr);
+  if (!g_scratch_ptr[device]) {
+    void* p = nullptr;
+    hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[device] = p;
+  }
+  *out = g_scratch_ptr[device];
+  return hipSuccess;
+}
+
+size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+// Where one attention call keeps its scratch: the prepared queries and the
+// split-KV partials.
+struct Work {
+  void* qrot;
+  float* o_part;
+  float* lse_part;
+};
 
 struct ProfRec {
   int kind;
@@ -66,6 +104,7 @@ struct gca_cache {
   float* o_part = nullptr;
   float* lse_part = nullptr;
   void* qrot = nullptr;  // prepared queries (rotated, scaled) of the current attention call
+  void* static_scratch = nullptr;  // this device's copy of `scratch` (gca_step_static)
   // tiles of a first-dispatched split per tile of a second-dispatched one
   float split_ratio = 1.7f;
   bool sel_valid = false;
@@ -222,10 +261,10 @@ gca::EvictArgs evict_args(gca_cache* c, const gca::EvictStep& st) {
 
 // The attention's queries: rotated when rope = 1 and scaled by
 // sm_scale * log2(e), rounded once, into the query workspace.
-gca::RopeArgs query_args(gca_cache* c, int64_t frame_idx, const void* q, int nf = 1) {
+gca::RopeArgs query_args(gca_cache* c, int64_t frame_idx, const void* q, void* dst, int nf = 1) {
   gca::RopeArgs ra;
   ra.x = q;
-  ra.y = c->qrot;
+  ra.y = dst;
   ra.frame = frame_idx;
   ra.nf = nf;
   ra.T = c->g.T;
@@ -236,33 +275,73 @@ gca::RopeArgs query_args(gca_cache* c, int64_t frame_idx, const void* q, int nf 
   return ra;
 }
 
-// Attention over the gather list already built for `st` (queries qa of nf
-// stacked frames already prepared by query_args), then the split merge.
-int attend_launch(gca_cache* c, int64_t frame_idx, const void* qa, void* out, float* lse,
-                  const gca::SelectStep& st, hipStream_t s, int nf = 1) {
+// Split count of an attention call over n_sel gather entries for nf frames of
+// queries: about two workgroups per compute unit, at most kMaxSplits / nf
+// (the cache's split workspace holds kMaxSplits partials of one frame's rows),
+// at least two tiles per split.
+struct Split {
+  int n_tiles, qtiles, S, tps;
+};
+Split split_of(const gca_cache* c, int n_sel, int nf) {
   const gca::Geometry& g = c->g;
-  const int Tq = nf * g.T;
-  int ept = gca::kKeysPerTile / g.P;
-  int n_tiles = (st.n_sel + ept - 1) / ept;
-  int qpw = gca::queries_per_wg(g.dtype);
-  int qtiles = (Tq + qpw - 1) / qpw;
-  // split the context so that about two workgroups run per compute unit; the
-  // split workspace holds kMaxSplits partials of one frame's rows
-  int base = qtiles * g.H;
+  Split sp;
+  const int ept = gca::kKeysPerTile / g.P;
+  sp.n_tiles = (n_sel + ept - 1) / ept;
+  sp.qtiles = (nf * g.T + gca::queries_per_wg(g.dtype) - 1) / gca::queries_per_wg(g.dtype);
+  const int base = sp.qtiles * g.H;
   int S = (2 * c->num_cu + base - 1) / base;
   S = std::min(S, kMaxSplits / nf);
-  S = std::min(S, std::max(1, n_tiles / 2));
+  S = std::min(S, std::max(1, sp.n_tiles / 2));
   S = std::max(S, 1);
-  int tps = (n_tiles + S - 1) / S;
-  S = (n_tiles + tps - 1) / tps;
+  sp.tps = (sp.n_tiles + S - 1) / S;
+  sp.S = (sp.n_tiles + sp.tps - 1) / sp.tps;
+  return sp;
+}
+
+// Scratch bytes of one attention call: the prepared queries of nf frames and,
+// when split, the partials.
+size_t work_bytes(const gca_cache* c, const Split& sp, int nf) {
+  const gca::Geometry& g = c->g;
+  const size_t rows = (size_t)nf * g.T * g.H;
+  size_t b = align256(rows * g.D * c->esize);
+  if (sp.S > 1) b += align256(sizeof(float) * rows * g.D * sp.S) + align256(sizeof(float) * rows * sp.S);
+  return b;
+}
+
+// The scratch of one call laid out in the static array: queries, partials,
+// partial LSEs, each 256-byte aligned.
+Work static_work(const gca_cache* c, const Split& sp, int nf) {
+  const gca::Geometry& g = c->g;
+  const size_t rows = (size_t)nf * g.T * g.H;
+  char* p = (char*)c->static_scratch;
+  Work w;
+  w.qrot = p;
+  p += align256(rows * g.D * c->esize);
+  w.o_part = (float*)p;
+  p += align256(sizeof(float) * rows * g.D * std::max(sp.S, 1));
+  w.lse_part = (float*)p;
+  return w;
+}
+
+Work own_work(const gca_cache* c) { return Work{c->qrot, c->o_part, c->lse_part}; }
+
+// Attention over the gather list already built for `st` (queries of nf
+// stacked frames already prepared into w.qrot by query_args), then the split
+// merge.
+int attend_launch(gca_cache* c, int64_t frame_idx, void* out, float* lse, const gca::SelectStep& st,
+                  hipStream_t s, const Work& w, int nf = 1) {
+  const gca::Geometry& g = c->g;
+  const int Tq = nf * g.T;
+  const Split sp = split_of(c, st.n_sel, nf);
+  const int n_tiles = sp.n_tiles, S = sp.S;
   gca::AttnArgs a;
-  a.q = qa;
+  a.q = w.qrot;
   a.kpool = c->kpool;
   a.vpool = c->vpool;
   a.sel_page = c->sel_page;
   a.sel_len = c->sel_len;
-  a.o_part = c->o_part;
-  a.lse_part = c->lse_part;
+  a.o_part = w.o_part;
+  a.lse_part = w.lse_part;
   a.out = out;
   a.lse = lse;
   a.frame = frame_idx;
@@ -271,9 +350,9 @@ int attend_launch(gca_cache* c, int64_t frame_idx, const void* qa, void* out, fl
   a.P = g.P;
   a.n_sel = st.n_sel;
   a.n_tiles = n_tiles;
-  a.tiles_per_split = tps;
+  a.tiles_per_split = sp.tps;
   a.S = S;
-  a.n_qtiles = qtiles;
+  a.n_qtiles = sp.qtiles;
   a.n_units = g.H * S;
   a.out_bf16 = g.out_dtype == GCA_BF16;
   a.head_major = g.H % gca::kNumXcd == 0;
@@ -294,8 +373,8 @@ int attend_launch(gca_cache* c, int64_t frame_idx, const void* qa, void* out, fl
   }
   if (S > 1) {
     gca::MergeArgs m;
-    m.o_part = c->o_part;
-    m.lse_part = c->lse_part;
+    m.o_part = w.o_part;
+    m.lse_part = w.lse_part;
     m.out = out;
     m.lse = lse;
     m.rows = Tq * g.H;
@@ -416,6 +495,8 @@ int gca_cache_create(const gca_config* cfg, gca_cache** out) {
     c->tabs.num_special = g.num_special;
     c->tabs.grid_w = g.grid_w;
   }
+  if ((e = static_scratch(c->device, &c->static_scratch)) != hipSuccess)
+    return fail(e, "static scratch address");
   if ((e = hipDeviceSynchronize()) != hipSuccess) return fail(e, "create sync");
   *out = c;
   return GCA_OK;
@@ -526,13 +607,13 @@ int gca_attend(gca_cache* c, int64_t frame_idx, const void* q, void* out, float*
   {
     // gather list and prepared queries from one launch
     Prof p(c, 2, s);
-    GCA_HIP(gca::launch_prepare(g.dtype, select_args(c, st), query_args(c, frame_idx, q), s),
+    GCA_HIP(gca::launch_prepare(g.dtype, select_args(c, st), query_args(c, frame_idx, q, c->qrot), s),
             "prepare kernel launch");
   }
   c->sel_valid = true;
   c->sel_n = st.n_sel;
   c->sel_ctx = st.n_ctx;
-  return attend_launch(c, frame_idx, c->qrot, out, lse, st, s);
+  return attend_launch(c, frame_idx, out, lse, st, s, own_work(c));
 }
 
 int gca_attend_frames(gca_cache* c, int64_t first_frame, int32_t n_frames, const void* q, void* out,
@@ -548,13 +629,14 @@ int gca_attend_frames(gca_cache* c, int64_t first_frame, int32_t n_frames, const
   gca::SelectStep st = c->plan.select();
   {
     Prof p(c, 2, s);
-    GCA_HIP(gca::launch_prepare(g.dtype, select_args(c, st), query_args(c, first_frame, q, n_frames), s),
+    GCA_HIP(gca::launch_prepare(g.dtype, select_args(c, st), query_args(c, first_frame, q, c->qrot, n_frames),
+                                s),
             "prepare kernel launch");
   }
   c->sel_valid = true;
   c->sel_n = st.n_sel;
   c->sel_ctx = st.n_ctx;
-  return attend_launch(c, first_frame + n_frames - 1, c->qrot, out, lse, st, s, n_frames);
+  return attend_launch(c, first_frame + n_frames - 1, out, lse, st, s, own_work(c), n_frames);
 }
 
 int gca_rollback_last_frame(gca_cache* c, int64_t frame_idx, gca_stream_t stream) {
@@ -569,8 +651,14 @@ int gca_rollback_last_frame(gca_cache* c, int64_t frame_idx, gca_stream_t stream
   return GCA_OK;
 }
 
-int gca_step(gca_cache* c, int64_t frame_idx, const void* k, const void* v, const void* q, void* out,
-             float* lse, uint32_t flags, gca_stream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// One frame of the loop (gca_step), its attention scratch in the cache's own
+// workspace or, with use_static, in this device's copy of `scratch`.
+int step_impl(gca_cache* c, int64_t frame_idx, const void* k, const void* v, const void* q, void* out,
+              float* lse, uint32_t flags, gca_stream_t stream, bool use_static) {
   if (!c || !aligned16(k) || !aligned16(v) || !aligned16(q) || !aligned16(out) ||
       (lse && ((uintptr_t)lse & 3)) || (flags & ~GCA_STEP_KEYFRAME))
     return GCA_ERR_INVALID_ARGUMENT;
@@ -590,19 +678,42 @@ int gca_step(gca_cache* c, int64_t frame_idx, const void* k, const void* v, cons
   }
   if ((rc = p.check_attend(frame_idx))) return rc;
   if (!key && (rc = p.check_rollback(frame_idx))) return rc;
+  const gca::SelectStep st = p.select();
+  Work w = own_work(c);
+  if (use_static) {
+    const Split sp = split_of(c, st.n_sel, 1);
+    const size_t need = work_bytes(c, sp, 1);
+    if (need > kStaticScratchBytes) {
+      char buf[192];
+      std::snprintf(buf, sizeof buf, "gca_step_static: the step needs %zu bytes of scratch, the static array holds %zu",
+                    need, kStaticScratchBytes);
+      g_last_error = buf;
+      return GCA_ERR_CAPACITY;
+    }
+    w = static_work(c, sp, 1);
+  }
 
   hipStream_t s = (hipStream_t)stream;
   if (ev.size() > 1) {
-    // several evictions depend on one another: the individual calls
+    // several evictions depend on one another: the individual calls, then the
+    // attention with this step's scratch
     if ((rc = gca_append_frame(c, frame_idx, k, v, 0, stream))) return rc;
     if ((rc = gca_evict_compact(c, stream))) return rc;
-    return gca_attend(c, frame_idx, q, out, lse, stream);
+    const gca::SelectStep st2 = c->plan.select();
+    {
+      Prof pr(c, 2, s);
+      GCA_HIP(gca::launch_prepare(g.dtype, select_args(c, st2), query_args(c, frame_idx, q, w.qrot), s),
+              "prepare kernel launch");
+    }
+    c->sel_valid = true;
+    c->sel_n = st2.n_sel;
+    c->sel_ctx = st2.n_ctx;
+    return attend_launch(c, frame_idx, out, lse, st2, s, w);
   }
-  const gca::SelectStep st = p.select();
   gca::AppendArgs aa = append_args(c, as, k, v);
   gca::EvictArgs ea{};
   if (!ev.empty()) ea = evict_args(c, ev[0]);
-  gca::RopeArgs ra = query_args(c, frame_idx, q);
+  gca::RopeArgs ra = query_args(c, frame_idx, q, w.qrot);
   gca::SelectArgs sa = select_args(c, st);
   sa.newest_pos = as.ring_pos % g.N;
   if (!ev.empty()) {
@@ -618,13 +729,27 @@ int gca_step(gca_cache* c, int64_t frame_idx, const void* k, const void* v, cons
   c->sel_valid = true;
   c->sel_n = st.n_sel;
   c->sel_ctx = st.n_ctx;
-  rc = attend_launch(c, frame_idx, c->qrot, out, lse, st, s);
+  rc = attend_launch(c, frame_idx, out, lse, st, s, w);
   if (rc) return rc;
   if (!key) {
     c->plan.commit_rollback();
     c->sel_valid = false;
   }
   return GCA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gca_step(gca_cache* c, int64_t frame_idx, const void* k, const void* v, const void* q, void* out,
+             float* lse, uint32_t flags, gca_stream_t stream) {
+  return step_impl(c, frame_idx, k, v, q, out, lse, flags, stream, false);
+}
+
+int gca_step_static(gca_cache* c, int64_t frame_idx, const void* k, const void* v, const void* q, void* out,
+                    float* lse, uint32_t flags, gca_stream_t stream) {
+  return step_impl(c, frame_idx, k, v, q, out, lse, flags, stream, true);
 }
 
 int gca_rope3d(gca_cache* c, int64_t frame_idx, const void* x, void* y, gca_stream_t stream) {

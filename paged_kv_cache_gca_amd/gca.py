@@ -24,6 +24,7 @@ GCA_ERR_UNSUPPORTED = -6
 GCA_F32, GCA_BF16 = 0, 1
 GCA_APPEND_TEMP = 1
 STEP_KEYFRAME = 1
+STATIC_SCRATCH_BYTES = 64 << 20  # GCA_STATIC_SCRATCH_BYTES
 KIND = {"append": 0, "evict": 1, "select": 2, "attn": 3, "merge": 4, "rope": 5, "update": 6}
 
 
@@ -83,6 +84,7 @@ def _load():
         "gca_append_frames": [vp, i64, i32, vp, vp, vp],
         "gca_rollback_last_frame": [vp, i64, vp],
         "gca_step": [vp, i64, vp, vp, vp, vp, vp, u32, vp],
+        "gca_step_static": [vp, i64, vp, vp, vp, vp, vp, u32, vp],
         "gca_select": [vp, vp],
         "gca_rope3d": [vp, i64, vp, vp, vp],
         "gca_query": [vp, C.POINTER(gca_info)],
@@ -348,6 +350,12 @@ class Cache:
         self._validate(out=out, lse=lse, k=k, v=v, q=q)
         return _lib.gca_step(self.h, frame, _ptr(k), _ptr(v), _ptr(q), _ptr(out), _ptr(lse),
                              STEP_KEYFRAME if keyframe else 0, _stream(stream))
+
+    def step_static(self, frame: int, k, v, q, out, lse=None, keyframe: bool = True, stream=None) -> int:
+        """step() with its scratch in the library's fixed device array (no allocation)"""
+        self._validate(out=out, lse=lse, k=k, v=v, q=q)
+        return _lib.gca_step_static(self.h, frame, _ptr(k), _ptr(v), _ptr(q), _ptr(out), _ptr(lse),
+                                    STEP_KEYFRAME if keyframe else 0, _stream(stream))
 
     def select(self, stream=None) -> int:
         return _lib.gca_select(self.h, _stream(stream))
