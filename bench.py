@@ -16,7 +16,13 @@ back-to-back batches for their HBM roofline (`append_compact`).  MFMA busy and
 HBM traffic come from the committed rocprofv3 counter summary of the same
 kernel source; the other kernels' durations from a rocprofv3 kernel trace.
 
+The headline line is the 64-frame stream at page size 16; `configs` holds the
+same measurements for the three long streams (1,000 frames with a 64-frame
+window, 10,000 drifting frames with keyframe interval 4, the 20,000-frame
+12-frame ring), each with its own CPU baseline.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                       [--no-configs] [--no-cpu-baseline] [--stream-only]
 """
 from __future__ import annotations
 
@@ -45,8 +51,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=64)
     ap.add_argument("--stream-only", action="store_true",
-                    help="skip the scale-phase and camera-head measurements (counter runs that "
-                         "average per stream launch)")
+                    help="skip the scale-phase, camera-head and long-stream measurements (counter runs "
+                         "that average per stream launch)")
+    ap.add_argument("--no-configs", action="store_true", help="skip the long-stream lines")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 256 MiB device-to-device copy (counter calibration)")
     return ap.parse_args()
@@ -81,6 +88,59 @@ def counters_from_profiles(kh: str) -> dict:
     return d if d.get("kernel_hash") == kh else {}
 
 
+def stage_frames(w, fs, dt, n_stage):
+    """Device copies of the stream's inputs, made before any timing: the
+    n_stage distinct query frames, and the key/value frames -- the same
+    n_stage for a cycled stream, every frame for a drifting one (the per-frame
+    offsets of the random walk added in float32 to the float32 base draws on
+    the device and rounded once, as the generator does on the host)."""
+    import numpy as np
+    import torch
+    from paged_kv_cache_gca_amd.synth import TENSOR_K, TENSOR_V
+    print(f"[bench] staging {n_stage} distinct frames of {w.name}", file=sys.stderr, flush=True)
+    Q, K, V = [], [], []
+    for f in range(n_stage):
+        Q.append(torch.from_numpy(fs.q(f)).to(dt).cuda())
+        if not w.drift_sigma:
+            k, v = fs.kv(f)
+            K.append(torch.from_numpy(k).to(dt).cuda())
+            V.append(torch.from_numpy(v).to(dt).cuda())
+    if w.drift_sigma:
+        bk = [torch.from_numpy(fs.base(f, TENSOR_K)).cuda() for f in range(n_stage)]
+        bv = [torch.from_numpy(fs.base(f, TENSOR_V)).cuda() for f in range(n_stage)]
+        mu = np.stack([np.stack(fs.drift(f)) for f in range(w.n_frames)]).astype(np.float32)
+        mu = torch.from_numpy(mu).cuda()                       # [n_frames][2][H][D]
+        print(f"[bench] {w.n_frames} drifting key/value frames on the device", file=sys.stderr, flush=True)
+        for f in range(w.n_frames):
+            i = f % n_stage
+            K.append((bk[i] + mu[f, 0][None]).to(dt))
+            V.append((bv[i] + mu[f, 1][None]).to(dt))
+        # the device rounding is the generator's: a few frames compared bit for bit
+        for f in (0, 1, w.n_frames // 2, w.n_frames - 1):
+            k, v = fs.kv(f)
+            assert torch.equal(K[f].cpu(), torch.from_numpy(k).to(dt)), f
+            assert torch.equal(V[f].cpu(), torch.from_numpy(v).to(dt)), f
+        del bk, bv, mu
+    torch.cuda.synchronize()
+    return Q, K, V
+
+
+def plan_n_ctx(w):
+    """Context length of every frame of the stream (data independent), from the host planner."""
+    from paged_kv_cache_gca_amd import gca
+    plan = gca.Plan(gca.Config.from_workload(w))
+    n_ctx = []
+    for f in range(w.n_frames):
+        key = w.is_keyframe(f)
+        plan.append(f, temp=not key)
+        if key:
+            plan.evict()
+        n_ctx.append(plan.query().n_ctx)
+        if not key:
+            plan.rollback(f)
+    return n_ctx
+
+
 def run_gpu(w, steps, warmup):
     import numpy as np
     import torch
@@ -92,15 +152,7 @@ def run_gpu(w, steps, warmup):
     dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     fs = FrameStream(w.seed, w.T, w.H, w.D, w.dtype, n_base=w.n_base, drift_sigma=w.drift_sigma)
     n_stage = w.n_frames if w.n_base is None else min(w.n_frames, w.n_base)
-    if w.drift_sigma:
-        raise SystemExit("drifting streams are parity cases, not bench lines")
-    print(f"[bench] staging {n_stage} distinct frames of {w.name}", file=sys.stderr, flush=True)
-    Q, K, V = [], [], []
-    for f in range(n_stage):
-        k, v = fs.kv(f)
-        Q.append(torch.from_numpy(fs.q(f)).to(dt).cuda())
-        K.append(torch.from_numpy(k).to(dt).cuda())
-        V.append(torch.from_numpy(v).to(dt).cuda())
+    Q, K, V = stage_frames(w, fs, dt, n_stage)
     cache = gca.Cache(gca.Config.from_workload(w))
     out = torch.empty((w.T, w.H, w.D), dtype=torch.float32, device="cuda")
     lse = torch.empty((w.T, w.H), dtype=torch.float32, device="cuda")
@@ -120,7 +172,8 @@ def run_gpu(w, steps, warmup):
                 tail_ev.append(e)
             i = f % n_stage
             # append (+ evict) + attend (+ rollback): one update launch, then attention
-            rc = cache.step(f, K[i], V[i], Q[i], out, lse, keyframe=w.is_keyframe(f), stream=stream)
+            rc = cache.step(f, K[f % len(K)], V[f % len(V)], Q[i], out, lse, keyframe=w.is_keyframe(f),
+                            stream=stream)
             if rc != 0:
                 raise RuntimeError(f"frame {f}: {gca.status_string(rc)}")
         if mark_tail:
@@ -128,17 +181,7 @@ def run_gpu(w, steps, warmup):
             e.record(stream)
             tail_ev.append(e)
 
-    # context length per frame (data independent) from the host planner
-    plan = gca.Plan(gca.Config.from_workload(w))
-    n_ctx = []
-    for f in range(w.n_frames):
-        key = w.is_keyframe(f)
-        plan.append(f, temp=not key)
-        if key:
-            plan.evict()
-        n_ctx.append(plan.query().n_ctx)
-        if not key:
-            plan.rollback(f)
+    n_ctx = plan_n_ctx(w)
     flop_stream = float(sum(4.0 * w.T * w.H * w.D * n for n in n_ctx))
 
     print(f"[bench] warmup {warmup} streams", file=sys.stderr, flush=True)
@@ -178,7 +221,7 @@ def run_gpu(w, steps, warmup):
 
     def appends():  # TEMP appends of frames 0..n-1 on an empty cache, each rolled back (host only)
         for f in range(w.n_frames):
-            if cache.append_frame(f, K[f % n_stage], V[f % n_stage], temp=True, stream=stream) != 0 or \
+            if cache.append_frame(f, K[f % len(K)], V[f % len(V)], temp=True, stream=stream) != 0 or \
                     cache.rollback_last_frame(f, stream) != 0:
                 raise RuntimeError("append batch failed")
 
@@ -197,12 +240,12 @@ def run_gpu(w, steps, warmup):
         if cache.reset(stream) != 0:
             raise RuntimeError("reset failed")
         for f in kf[:fill]:
-            if cache.append_frame(f, K[f % n_stage], V[f % n_stage], stream=stream) != 0:
+            if cache.append_frame(f, K[f % len(K)], V[f % len(V)], stream=stream) != 0:
                 raise RuntimeError("fill failed")
 
         def pairs():
             for f in kf[fill:]:
-                if cache.append_frame(f, K[f % n_stage], V[f % n_stage], stream=stream) != 0 or \
+                if cache.append_frame(f, K[f % len(K)], V[f % len(V)], stream=stream) != 0 or \
                         cache.evict_compact(stream) != 0:
                     raise RuntimeError("eviction batch failed")
         torch.cuda.synchronize()
@@ -293,7 +336,7 @@ def scale_phase_cpu(w, nf=8, n_rows=8):
     import oracle
     from paged_kv_cache_gca_amd.synth import FrameStream
 
-    threads = os.cpu_count() or 1
+    threads = _cpu_threads()
     fs = FrameStream(w.seed, w.T, w.H, w.D, w.dtype, n_base=w.n_base)
     cfg = oracle.OracleConfig(T=w.T, H=w.H, D=w.D, P=w.P, dtype=w.dtype, A=nf, W=w.W, C=w.C,
                               rope=w.rope, num_special=w.num_special, grid_h=w.grid_h,
@@ -359,57 +402,114 @@ def append_compact_line(w, kern):
     return out
 
 
-def run_cpu_baseline(w, rows_per_frame):
-    """The CPU oracle on a bounded sample of the same stream (test infrastructure)."""
+def _cpu_threads() -> int:
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:
+        return os.cpu_count() or 1
+
+
+def _cpu_model():
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def run_cpu_baseline(w, n_ctx):
+    """The CPU oracle (test infrastructure, untuned) on a bounded sample of the
+    same stream, on the host cores: bookkeeping (append, evict, rollback with
+    the frame's data) for every frame up to the second sampled frame, timed per
+    frame; attention for all T query rows and all heads at two sampled frames
+    with different context lengths.  The oracle's attention cost per frame is
+    linear in n_ctx (two passes over the context per row and head), so the two
+    frames give a + b n_ctx, which is applied to every frame of the stream
+    (n_ctx from the planner) together with the mean bookkeeping time."""
     import numpy as np
 
     import oracle
     from paged_kv_cache_gca_amd.synth import FrameStream
 
-    threads = os.cpu_count() or 1
+    threads = _cpu_threads()
     fs = FrameStream(w.seed, w.T, w.H, w.D, w.dtype, n_base=w.n_base, drift_sigma=w.drift_sigma)
     cfg = oracle.OracleConfig(T=w.T, H=w.H, D=w.D, P=w.P, dtype=w.dtype, A=w.A, W=w.W, C=w.C,
                               rope=w.rope, num_special=w.num_special, grid_h=w.grid_h,
                               grid_w=w.grid_w, rope_theta=w.rope_theta, max_frames=w.n_frames)
     c = oracle.OracleCache(cfg)
-    rows = np.linspace(0, w.T - 1, rows_per_frame).astype(np.int32)
-    n_frames = min(w.n_frames, 64)
+    # sampled frames: one early, one once the window has filled (at most the stream's end)
+    fb = min(w.n_frames - 1, (w.A + w.W + 1) * w.keyframe_interval)
+    fa = min(fb // 4, w.n_frames - 1)
     t_book = 0.0
-    t_attn = 0.0
-    t_one = None
-    for f in range(n_frames):
+    timed = {}
+    for f in range(fb + 1):
         key = w.is_keyframe(f)
         k, v = fs.kv(f)
-        q = fs.q(f)
         a = time.perf_counter()
         c.append(f, k, v, temp=not key)
         if key:
             c.evict()
-        b = time.perf_counter()
-        c.attend(f, q, rows=rows[:1], threads=threads)
-        m = time.perf_counter()
-        c.attend(f, q, rows=rows, threads=threads)
-        e = time.perf_counter()
+        t_book += time.perf_counter() - a
+        if f in (fa, fb):
+            q = fs.q(f)
+            a = time.perf_counter()
+            c.attend(f, q, threads=threads)
+            timed[f] = (time.perf_counter() - a, c.n_ctx())
         if not key:
+            a = time.perf_counter()
             c.rollback(f)
-        t_book += b - a
-        one = m - b                      # fixed part: rotate Q, materialise context
-        per_row = max(0.0, (e - m) - one) / max(1, len(rows) - 1)
-        t_attn += one + per_row * w.T    # all T query rows
-    est = t_book + t_attn
-    model = None
-    try:
-        for ln in open("/proc/cpuinfo"):
-            if ln.startswith("model name"):
-                model = ln.split(":", 1)[1].strip()
-                break
-    except OSError:
-        pass
-    return dict(value=n_frames / est, unit="frames/s/layer", cores=threads, kind="oracle", cpu_model=model,
-                sample=(f"first {n_frames} frames of {w.name}: every append/evict plus attention "
-                        f"for {len(rows)} of {w.T} query rows per frame (and 1 row, to separate "
-                        f"the fixed cost); full-row time scaled linearly in rows; "
-                        f"estimated {est:.1f} s for the {n_frames} frames"))
+            t_book += time.perf_counter() - a
+    book = t_book / (fb + 1)
+    (ta, na), (tb, nb) = timed[fa], timed[fb]
+    slope = (tb - ta) / (nb - na) if nb != na else tb / nb
+    icpt = max(0.0, tb - slope * nb)
+    est = w.n_frames * book + sum(icpt + slope * n for n in n_ctx)
+    return dict(value=w.n_frames / est, unit="frames/s/layer", cores=threads, kind="oracle",
+                cpu_model=_cpu_model(),
+                full_row_frames={str(fa): {"n_ctx": na, "s": round(ta, 3)},
+                                 str(fb): {"n_ctx": nb, "s": round(tb, 3)}},
+                bookkeeping_s_per_frame=round(book, 5),
+                sample=(f"{w.name}: bookkeeping (append/evict/rollback with data) of frames 0..{fb}, "
+                        f"attention for all {w.T} query rows x {w.H} heads at frames {fa} and {fb} "
+                        f"(n_ctx {na} and {nb}); whole stream modelled as {w.n_frames} x the mean "
+                        f"bookkeeping time plus a + b*n_ctx per frame from those two frames: "
+                        f"{est:.1f} s for the {w.n_frames} frames"))
+
+
+def stream_line(w, steps, warmup, cpu: bool):
+    """frames/s/layer, attention roofline, steady state and append/compaction
+    HBM fractions of one stream workload, plus its CPU baseline."""
+    r = run_gpu(w, steps, warmup)
+    attn_ms, attn_n = r["kern"]["attn"]
+    flop_per_launch = r["flop_stream"] / w.n_frames
+    avg_attn_s = attn_ms / 1e3 / max(attn_n, 1)
+    achieved = flop_per_launch / avg_attn_s / 1e12
+    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_MFMA_TFLOPS
+    line = {
+        "workload": w.name,
+        "value": round(steps * w.n_frames / r["seconds"], 2),
+        "unit": "frames/s/layer",
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(r["seconds"] * 1e3 / steps, 4),
+        "config": {"tokens_per_frame": w.T, "heads": w.H, "head_dim": w.D, "page_size": w.P,
+                   "frames_per_step": w.n_frames, "anchor": w.A, "window": w.W, "compact": w.C,
+                   "keyframe_interval": w.keyframe_interval, "drift_sigma": w.drift_sigma},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(achieved / peak, 4)},
+        "steady_state": {"frames": list(r["tail_frames"]), "value": round(r["tail_fps"], 2),
+                         "unit": "frames/s/layer"},
+        "append_compact": append_compact_line(w, r["kern"]),
+        "attn_ms_avg": round(attn_ms / max(attn_n, 1), 5),
+        "mean_n_ctx": round(sum(r["n_ctx"]) / len(r["n_ctx"]), 1),
+        "attn_flop_per_launch": flop_per_launch,
+    }
+    if cpu:
+        print(f"[bench] cpu baseline (oracle) {w.name}", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = run_cpu_baseline(w, r["n_ctx"])
+    return line, r
 
 
 def main():
@@ -422,45 +522,35 @@ def main():
         sys.exit(2)
     from paged_kv_cache_gca_amd import workloads as WL
     w = {x.name: x for x in WL.ALL}[args.workload]
-    r = run_gpu(w, args.steps, args.warmup)
-    frames = args.steps * w.n_frames
-    value = frames / r["seconds"]
-    attn_ms, attn_n = r["kern"]["attn"]
-    flop_per_launch = r["flop_stream"] / w.n_frames
-    avg_attn_s = attn_ms / 1e3 / max(attn_n, 1)
-    achieved = flop_per_launch / avg_attn_s / 1e12
-    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_MFMA_TFLOPS
+    cpu = not args.no_cpu_baseline
+    head, r = stream_line(w, args.steps, args.warmup, cpu=False)
     kh = kernel_hash()
     ctr = counters_from_profiles(kh)
     traffic = ctr.get("bytes_per_launch")
+    head["roofline"]["traffic"] = traffic if traffic is None else round(traffic)
 
     line = {
         "metric": METRIC,
-        "value": round(value, 2),
+        "value": head["value"],
         "unit": "frames/s/layer",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(r["seconds"] * 1e3 / args.steps, 4),
+        "ms_per_step": head["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": w.dtype,
         "data": "synthetic",
-        "config": {"workload": w.name, "tokens_per_frame": w.T, "heads": w.H, "head_dim": w.D,
-                   "page_size": w.P, "frames_per_step": w.n_frames, "anchor": w.A, "window": w.W,
-                   "compact": w.C, "keyframe_interval": w.keyframe_interval, "rope": "3d" if w.rope else "none",
-                   "parallelism": "none (1 GPU)"},
-        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
-                     "frac": round(achieved / peak, 4),
-                     "traffic": (traffic if traffic is None else round(traffic))},
-        "steady_state": {"frames": list(r["tail_frames"]), "value": round(r["tail_fps"], 2),
-                         "unit": "frames/s/layer"},
+        "config": {"workload": w.name, **{k: v for k, v in head["config"].items() if k != "drift_sigma"},
+                   "rope": "3d" if w.rope else "none", "parallelism": "none (1 GPU)"},
+        "roofline": head["roofline"],
+        "steady_state": head["steady_state"],
         "mfma_busy": ctr.get("mfma_busy"),
-        "append_compact": append_compact_line(w, r["kern"]),
-        "attn_ms_avg": round(attn_ms / max(attn_n, 1), 5),
-        "mean_n_ctx": round(sum(r["n_ctx"]) / len(r["n_ctx"]), 1),
-        "attn_flop_per_launch": flop_per_launch,
+        "append_compact": head["append_compact"],
+        "attn_ms_avg": head["attn_ms_avg"],
+        "mean_n_ctx": head["mean_n_ctx"],
+        "attn_flop_per_launch": head["attn_flop_per_launch"],
         "kernel_hash": kh,
         "device": r["device"],
     }
@@ -469,13 +559,19 @@ def main():
         line["scale_phase"] = run_scale_phase(w)
         print("[bench] camera-head cache", file=sys.stderr, flush=True)
         line["camera_head"] = camera_line(WL.CAMERA_T1)
-    if not args.no_cpu_baseline:
+    if not args.stream_only and not args.no_configs and w is WL.FRAME1004_W16:
+        # the long streams: fewer timed passes (each is 1,000 to 20,000 frames)
+        line["configs"] = {}
+        for wl, st, wu in ((WL.STREAM1000_W64, 3, 1), (WL.STREAM10K_KF4, 1, 1), (WL.RING20K_W12, 1, 1)):
+            sub, _ = stream_line(wl, st, wu, cpu=cpu)
+            line["configs"][wl.name] = sub
+    if cpu:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
-        line["cpu_baseline"] = run_cpu_baseline(w, args.cpu_rows)
+        line["cpu_baseline"] = run_cpu_baseline(w, r["n_ctx"])
         if "scale_phase" in line:
             line["scale_phase"]["cpu_baseline"] = scale_phase_cpu(w, line["scale_phase"]["frames"])
         if "camera_head" in line:
-            line["camera_head"]["cpu_baseline"] = run_cpu_baseline(WL.CAMERA_T1, 1)
+            line["camera_head"]["cpu_baseline"] = run_cpu_baseline(WL.CAMERA_T1, plan_n_ctx(WL.CAMERA_T1))
     print(json.dumps(line), flush=True)
 
 

@@ -121,19 +121,46 @@ void rope_vec(const Cfg& c, long long frame, int tok, const double* x, double* y
 }
 
 // Rotate (if enabled) and round a whole frame [T][H][D] into storage values.
+// The rotation of a token is the same for every head: its cos/sin are
+// evaluated once per token (the values rope_vec would use).  Tokens are
+// independent, so blocks of them go to separate threads.
 std::vector<float> prepare(const Cfg& c, long long frame, const float* x, bool rotate) {
   size_t n = (size_t)c.T * c.H * c.D;
   std::vector<float> out(n);
-  std::vector<double> a(c.D), b(c.D);
-  for (int t = 0; t < c.T; ++t)
-    for (int h = 0; h < c.H; ++h) {
-      const float* src = x + ((size_t)t * c.H + h) * c.D;
-      for (int d = 0; d < c.D; ++d) a[d] = src[d];
-      if (rotate && c.rope) rope_vec(c, frame, t, a.data(), b.data());
-      else b = a;
-      float* dst = out.data() + ((size_t)t * c.H + h) * c.D;
-      for (int d = 0; d < c.D; ++d) dst[d] = (float)round_store(c, b[d]);
+  const bool rot = rotate && c.rope;
+  auto tokens = [&](int t0, int t1) {
+    std::vector<double> a(c.D), b(c.D), cs(c.D / 2), sn(c.D / 2);
+    for (int t = t0; t < t1; ++t) {
+      if (rot)
+        for (int j = 0; j < c.D / 2; ++j) {
+          double ang = rope_angle(c, frame, t, j);
+          cs[j] = std::cos(ang);
+          sn[j] = std::sin(ang);
+        }
+      for (int h = 0; h < c.H; ++h) {
+        const float* src = x + ((size_t)t * c.H + h) * c.D;
+        for (int d = 0; d < c.D; ++d) a[d] = src[d];
+        if (rot) {
+          for (int j = 0; j < c.D / 2; ++j) {
+            b[2 * j] = a[2 * j] * cs[j] - a[2 * j + 1] * sn[j];
+            b[2 * j + 1] = a[2 * j] * sn[j] + a[2 * j + 1] * cs[j];
+          }
+        } else {
+          b = a;
+        }
+        float* dst = out.data() + ((size_t)t * c.H + h) * c.D;
+        for (int d = 0; d < c.D; ++d) dst[d] = (float)round_store(c, b[d]);
+      }
     }
+  };
+  const int nt = (int)std::max(1u, std::min(16u, std::thread::hardware_concurrency()));
+  if (nt == 1 || (size_t)c.T * c.H < 4096) {
+    tokens(0, c.T);
+  } else {
+    std::vector<std::thread> pool;
+    for (int i = 0; i < nt; ++i) pool.emplace_back(tokens, c.T * i / nt, c.T * (i + 1) / nt);
+    for (auto& th : pool) th.join();
+  }
   return out;
 }
 

@@ -67,10 +67,12 @@ def normals(seed: int, slot: int, tensor: int, n: int, start: int = 0) -> np.nda
 def round_bf16(x32: np.ndarray) -> np.ndarray:
     """Round float32 values to the nearest bfloat16 (ties to even); returns float32."""
     x32 = np.ascontiguousarray(x32, dtype=np.float32)
-    u = x32.view(np.uint32).astype(np.uint64)
-    lsb = (u >> np.uint64(16)) & np.uint64(1)
-    r = (u + np.uint64(0x7FFF) + lsb) & np.uint64(0xFFFF0000)
-    out = r.astype(np.uint32).view(np.float32)
+    u = x32.view(np.uint32)
+    lsb = (u >> np.uint32(16)) & np.uint32(1)
+    # 32-bit arithmetic: the sum wraps only for NaN bit patterns, replaced below
+    with np.errstate(over="ignore"):
+        r = (u + np.uint32(0x7FFF) + lsb) & np.uint32(0xFFFF0000)
+    out = r.view(np.float32)
     nan = np.isnan(x32)
     if nan.any():
         out = out.copy()
