@@ -28,11 +28,11 @@ inline int padded_sel(int n_sel, int P) {
   return ((n_sel + ept - 1) / ept + 2) * ept;
 }
 
-// Rotary tables: (cos, sin) in float32, evaluated in float64 on the host.
+// Rotary tables: (cos, sin) in float64, evaluated on the host.
 struct RopeTabs {
-  const float2* t;  // [max_frames][nt]
-  const float2* h;  // [grid_h][nh]
-  const float2* w;  // [grid_w][nw]
+  const double2* t;  // [max_frames][nt]
+  const double2* h;  // [grid_h][nh]
+  const double2* w;  // [grid_w][nw]
   int nt, nh, nw;   // rotation pairs per axis block (time, row, column)
   int num_special, grid_w;
 };
@@ -91,7 +91,8 @@ struct SelectArgs {
 };
 
 struct AttnArgs {
-  const void* q;       // [Tq][H][D], rotated (3D RoPE) and scaled by sm_scale * log2(e)
+  const void* q;       // [Tq][H][D], rotated (3D RoPE) and rounded to the cache dtype
+  float qk_scale;      // sm_scale * log2(e): scores q'.k' times this are base-2 logits
   const void* kpool;   // [N][H][P][D]
   const void* vpool;   // [N][H][D][P]
   const int32_t* sel_page;
@@ -129,8 +130,7 @@ struct RopeArgs {
   int64_t frame;
   int nf;
   int T, H;
-  int rotate;   // 0: y = scale * x (no rotation)
-  float scale;  // 1 for keys; sm_scale * log2(e) for the attention's queries
+  int rotate;   // 0: y = x
   RopeTabs tabs;
 };
 

@@ -8,7 +8,7 @@
 //             and push the frame's pages to the ring tail
 //   k_select  gather list (page, valid tokens): anchor, window, trajectory
 //   k_prepare gather list plus the attention's prepared queries (rotated,
-//             scaled to base-2 logits, rounded once) in one launch
+//             rounded once) in one launch
 //   k_update  one frame's append, eviction, query preparation and gather
 //             list in one launch (the per-frame step)
 //   k_attn    paged flash attention: K/V pages staged in LDS, S^T = K Q^T and
@@ -47,13 +47,17 @@ __device__ inline bf16 from_f<bf16>(float x) { return (bf16)x; }  // round to ne
 // ---------------------------------------------------------------------------
 // 3D rotary embedding.  Pair j rotates dims (2j, 2j+1); pairs [0, nt) use the
 // frame index, [nt, nt+nh) the patch row, the rest the patch column; special
-// tokens sit at row 0, column 0.
+// tokens sit at row 0, column 0.  The rotation is evaluated in float64 from
+// float64 (cos, sin) and rounded once to the storage type: y0 = x0 c - x1 s,
+// y1 = x0 s + x1 c, each product and the sum rounded in float64 (no fused
+// multiply-add), then round to nearest even.
 
-// cos/sin of pairs `pair` and `pair` + 1 (pair even) in one 16-byte load: the
-// axis blocks have an even number of pairs (12, 10, 10 for D = 64), so both
-// lie next to each other in one table, at a 16-byte aligned offset.
-__device__ inline float4 rope_cs2(const RopeTabs& R, int64_t frame, int tok, int pair) {
-  const float2* p;
+// cos/sin of pairs `pair` and `pair` + 1 (pair even): the axis blocks have an
+// even number of pairs (12, 10, 10 for D = 64), so both lie next to each
+// other in one table.
+__device__ inline void rope_cs2(const RopeTabs& R, int64_t frame, int tok, int pair, double2& c0,
+                                double2& c1) {
+  const double2* p;
   if (pair < R.nt) {
     p = R.t + frame * R.nt + pair;
   } else {
@@ -66,38 +70,49 @@ __device__ inline float4 rope_cs2(const RopeTabs& R, int64_t frame, int tok, int
     pair -= R.nt;
     p = pair < R.nh ? R.h + row * R.nh + pair : R.w + col * R.nw + (pair - R.nh);
   }
-  return *(const float4*)p;
+  c0 = p[0];
+  c1 = p[1];
 }
 
-// One fixed operation sequence, so every kernel that rotates gives the same bits.
-__device__ inline void rotate(float x0, float x1, float2 cs, float& y0, float& y1) {
-  float a = x1 * cs.y;
-  float b = x1 * cs.x;
-  y0 = __builtin_fmaf(x0, cs.x, -a);
-  y1 = __builtin_fmaf(x0, cs.y, b);
+__device__ inline void rotate(double x0, double x1, double2 cs, double& y0, double& y1) {
+  y0 = __dsub_rn(__dmul_rn(x0, cs.x), __dmul_rn(x1, cs.y));
+  y1 = __dadd_rn(__dmul_rn(x0, cs.y), __dmul_rn(x1, cs.x));
 }
 
-// Rotated values times `scale` (exact for scale = 1), rounded once to T.
+// A float64 value rounded to the storage type, round to nearest even: for
+// bfloat16, to 8 significant bits (frexp, rint, ldexp), which a float holds
+// exactly and then converts to bfloat16 unchanged.
 template <typename T>
-__device__ inline void rotate_chunk(Vec16<T>& v, const RopeTabs& R, int64_t frame, int tok,
-                                    int first_pair, float scale = 1.f) {
+__device__ inline T round_store(double y);
+template <>
+__device__ inline float round_store<float>(double y) { return (float)y; }
+template <>
+__device__ inline bf16 round_store<bf16>(double y) {
+  if (y == 0.0 || !__builtin_isfinite(y)) return (bf16)(float)y;
+  int e;
+  const double m = __builtin_frexp(y, &e);
+  return (bf16)(float)__builtin_ldexp(__builtin_rint(m * 256.0), e - 8);
+}
+
+template <typename T>
+__device__ inline void rotate_chunk(Vec16<T>& v, const RopeTabs& R, int64_t frame, int tok, int first_pair) {
   constexpr int EPC = 16 / sizeof(T);
 #pragma unroll
   for (int m = 0; m < EPC / 2; m += 2) {
-    const float4 c4 = rope_cs2(R, frame, tok, first_pair + m);
+    double2 cs[2];
+    rope_cs2(R, frame, tok, first_pair + m, cs[0], cs[1]);
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      const float2 cs = u ? make_float2(c4.z, c4.w) : make_float2(c4.x, c4.y);
-      float y0, y1;
-      rotate(to_f(v.e[2 * (m + u)]), to_f(v.e[2 * (m + u) + 1]), cs, y0, y1);
-      v.e[2 * (m + u)] = from_f<T>(y0 * scale);
-      v.e[2 * (m + u) + 1] = from_f<T>(y1 * scale);
+      double y0, y1;
+      rotate((double)to_f(v.e[2 * (m + u)]), (double)to_f(v.e[2 * (m + u) + 1]), cs[u], y0, y1);
+      v.e[2 * (m + u)] = round_store<T>(y0);
+      v.e[2 * (m + u) + 1] = round_store<T>(y1);
     }
   }
 }
 
-// 16-byte chunk c of x -> y: rotated when a.rotate, times a.scale, rounded
-// once; chunks past the tensor are ignored
+// 16-byte chunk c of x -> y: rotated when a.rotate, else copied; chunks past
+// the tensor are ignored
 template <typename T>
 __device__ inline void rope_chunk(const RopeArgs& a, size_t c) {
   constexpr int EPC = 16 / sizeof(T);
@@ -109,12 +124,7 @@ __device__ inline void rope_chunk(const RopeArgs& a, size_t c) {
   int tok = row % a.T;
   Vec16<T> v;
   v.u = ((const uint4*)a.x)[c];
-  if (a.rotate) {
-    rotate_chunk<T>(v, a.tabs, a.frame + row / a.T, tok, part * EPC / 2, a.scale);
-  } else {
-#pragma unroll
-    for (int i = 0; i < EPC; ++i) v.e[i] = from_f<T>(to_f(v.e[i]) * a.scale);
-  }
+  if (a.rotate) rotate_chunk<T>(v, a.tabs, a.frame + row / a.T, tok, part * EPC / 2);
   ((uint4*)a.y)[c] = v.u;
 }
 template <typename T>
@@ -354,14 +364,21 @@ __global__ void k_ring_init(int32_t* ring, const int32_t* init, int N) {
 
 template <typename T>
 struct Mfma;
-typedef short shortx4 __attribute__((ext_vector_type(4)));
 
-// Seed operands: a rank-2 product fills a 32x32 S^T accumulator before the
-// K.Q^T MFMAs.  A holds, per key row, 1 in column 0 and the key's mask (1 for
-// a key past its page's valid length, else 0) in column 1; B holds, per query
-// column, the offset x in row 0 and -1e30 in row 1.  The product is x for a
-// valid key and x - 1e30 (exp2 of which is 0) for a masked one.
+__device__ inline floatx16 zero16() {
+  floatx16 z;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) z[i] = 0.f;
+  return z;
+}
+
+// Partial tiles start each 32-key block's S^T accumulators from a rank-1
+// mask product instead of zero: A holds, per key row, 1 for a key past its
+// gather entry's valid length (else 0) in column 0; B holds -1e30 in row 0 for
+// every query column.  A masked key's score is then about -1e30, its logit
+// -inf in effect, its P exactly 0.
 constexpr float kMaskedScore = -1e30f;
+typedef short shortx4 __attribute__((ext_vector_type(4)));
 
 template <>
 struct Mfma<bf16> {
@@ -373,30 +390,19 @@ struct Mfma<bf16> {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
   }
   __device__ static inline short bits(float x) { return __builtin_bit_cast(short, (bf16)x); }
-  __device__ static inline Seed seed_a(float mask, int hi) {
+  __device__ static inline Seed mask_a(bool masked, int hi) {
     Seed r = {0, 0, 0, 0};
-    if (hi == 0) {
-      r[0] = bits(1.f);
-      r[1] = bits(mask);
-    }
+    if (hi == 0) r[0] = bits(masked ? 1.f : 0.f);
     return r;
   }
-  __device__ static inline Seed seed_b(float x, int hi) {
+  __device__ static inline Seed mask_b(int hi) {
     Seed r = {0, 0, 0, 0};
-    if (hi == 0) {
-      r[0] = bits(x);
-      r[1] = bits(kMaskedScore);
-    }
+    if (hi == 0) r[0] = bits(kMaskedScore);
     return r;
   }
   __device__ static inline floatx16 mma_seed(Seed a, Seed b) {
-    floatx16 z;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) z[i] = 0.f;
-    return __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(a, b, z, 0, 0, 0);
+    return __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(a, b, zero16(), 0, 0, 0);
   }
-  // nearest value the seed operand holds exactly
-  __device__ static inline float exact(float x) { return (float)(bf16)x; }
 };
 template <>
 struct Mfma<float> {
@@ -407,15 +413,11 @@ struct Mfma<float> {
   __device__ static inline floatx16 mma(Frag a, Frag b, floatx16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
   }
-  __device__ static inline Seed seed_a(float mask, int hi) { return hi == 0 ? 1.f : mask; }
-  __device__ static inline Seed seed_b(float x, int hi) { return hi == 0 ? x : kMaskedScore; }
+  __device__ static inline Seed mask_a(bool masked, int hi) { return hi == 0 && masked ? 1.f : 0.f; }
+  __device__ static inline Seed mask_b(int hi) { return hi == 0 ? kMaskedScore : 0.f; }
   __device__ static inline floatx16 mma_seed(Seed a, Seed b) {
-    floatx16 z;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) z[i] = 0.f;
-    return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, z, 0, 0, 0);
+    return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, zero16(), 0, 0, 0);
   }
-  __device__ static inline float exact(float x) { return x; }
 };
 
 // bf16 tiles in LDS: 64 rows of 128 bytes (K: key rows of 64 dims; V^T: dim
@@ -489,6 +491,42 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 typedef int32_t i32x2 __attribute__((ext_vector_type(2)));
 
+// The EPT (= 1, 2 or 4) valid lengths of one tile's gather entries.
+template <int N>
+__device__ inline i32x4 load_lens(const int32_t* p) {
+  i32x4 v = {0, 0, 0, 0};
+  if constexpr (N == 4) {
+    v = *(const i32x4*)p;
+  } else if constexpr (N == 2) {
+    const i32x2 u = *(const i32x2*)p;
+    v.x = u.x;
+    v.y = u.y;
+  } else {
+    v.x = *p;
+  }
+  return v;
+}
+
+__device__ inline int pick(i32x4 v, int j) { return j == 0 ? v.x : j == 1 ? v.y : j == 2 ? v.z : v.w; }
+
+// Key `key` of a tile is masked when its slot lies past its gather entry's
+// valid length (a partial page, or padding).
+template <int P>
+__device__ inline bool key_masked(const i32x4& tl, int key) {
+  return (key % P) >= pick(tl, key / P);
+}
+
+// Whether any entry of the tile is partial (the same in every lane: made
+// wave-uniform so that full tiles skip the masks).
+template <int P>
+__device__ inline bool tile_partial(const i32x4& tl) {
+  constexpr int EPT = kKeysPerTile / P;
+  int any = 0;
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) any |= pick(tl, e) < P;
+  return __builtin_amdgcn_readfirstlane(any) != 0;
+}
+
 template <typename T, int P>
 struct TileLoader {
   static constexpr int EPC = 16 / sizeof(T);           // elements per 16-byte chunk
@@ -516,9 +554,8 @@ struct TileLoader {
   uint32_t page_bytes;
   int pg_k[NC], pg_v;         // page ids of the next tile
   u32x4 kr[NC], vr[NC];       // 16-byte chunks of the next tile (native vectors: plain loads)
-  int lens[2];                // valid lengths of the entries of keys l32 and 32 + l32 of the
-                              // tile whose page ids are held
-  int dlens[2];               // the same for the tile held in kr / vr
+  i32x4 tlen;                 // valid lengths of the EPT entries of the tile whose page ids are held
+  i32x4 dlen;                 // the same for the tile held in kr / vr
 
   __device__ void init(const T* kpool, const T* vpool, int h, int H, int tid) {
     page_bytes = (uint32_t)(H * P * kHeadDim * sizeof(T));
@@ -529,10 +566,10 @@ struct TileLoader {
   }
   // page ids and lengths of tile `tile` (the gather list is padded past its
   // end).  With several entries per tile each thread loads those of its own
-  // chunks and keys with plain vector loads, consumed a whole tile later when
-  // that tile's data loads are issued; with one entry per tile (P = 64) a
-  // scalar load through the constant address space (the list is not written
-  // during the launch) serves the whole wave.
+  // chunks with plain loads and all EPT lengths with one vector load,
+  // consumed a whole tile later when that tile's data loads are issued; with
+  // one entry per tile (P = 64) a scalar load through the constant address
+  // space (the list is not written during the launch) serves the whole wave.
   __device__ void fetch_pages(const AttnArgs& a, int tile, int tid) {
     if constexpr (EPT == 1) {
       typedef const __attribute__((address_space(4))) int32_t cint;
@@ -541,21 +578,17 @@ struct TileLoader {
 #pragma unroll
       for (int i = 0; i < NC; ++i) pg_k[i] = pg;
       pg_v = pg;
-      lens[0] = ln;
-      lens[1] = ln;
+      tlen = i32x4{ln, ln, ln, ln};
     } else {
       const int32_t* sp = a.sel_page + tile * EPT;
-      const int32_t* sl = a.sel_len + tile * EPT;
 #pragma unroll
       for (int i = 0; i < NC; ++i) pg_k[i] = sp[k_row(tid, i) / P];
       pg_v = sp[v_key0(tid) / P];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) lens[kb] = sl[(kb * 32 + (tid & 31)) / P];
+      tlen = load_lens<EPT>(a.sel_len + tile * EPT);
     }
   }
   __device__ void fetch_data(int tid) {
-    dlens[0] = lens[0];
-    dlens[1] = lens[1];
+    dlen = tlen;
 #pragma unroll
     for (int i = 0; i < NC; ++i) {
       kr[i] = *(const u32x4*)(kaddr[i] + (uint64_t)(uint32_t)pg_k[i] * page_bytes);
@@ -576,8 +609,6 @@ struct TileLoader {
     }
   }
 };
-
-__device__ inline int pick(i32x4 v, int j) { return j == 0 ? v.x : j == 1 ? v.y : j == 2 ? v.z : v.w; }
 
 // bf16 tiles go straight from HBM/L2 into LDS (global_load_lds: each lane's
 // 16 bytes land at the instruction's LDS base + lane * 16), three buffers
@@ -622,28 +653,9 @@ struct DmaLoader {
       voff[j] = (uint32_t)((d * P + (8 * c) % P) * 2);
     }
   }
-  template <int N>
-  __device__ static i32x4 load_n(const int32_t* p) {
-    i32x4 v = {0, 0, 0, 0};
-    if constexpr (N == 4) {
-      v = *(const i32x4*)p;
-    } else if constexpr (N == 2) {
-      const i32x2 u = *(const i32x2*)p;
-      v.x = u.x;
-      v.y = u.y;
-    } else {
-      v.x = *p;
-    }
-    return v;
-  }
   __device__ void fetch(const AttnArgs& a, int tile, Ids& x) const {
-    x.pg = load_n<EPT>(a.sel_page + tile * EPT);
-    x.ln = load_n<EPT>(a.sel_len + tile * EPT);
-  }
-  // entry lengths of keys l32 and 32 + l32
-  __device__ static void lens_of(const Ids& x, int l32, int (&out)[2]) {
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) out[kb] = pick(x.ln, (kb * 32 + l32) / P);
+    x.pg = load_lens<EPT>(a.sel_page + tile * EPT);
+    x.ln = load_lens<EPT>(a.sel_len + tile * EPT);
   }
   __device__ void issue(const char* kpool, const char* vpool, const Ids& x, char* buf, int w) const {
     typedef __attribute__((address_space(3))) void lds_t;
@@ -771,63 +783,58 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
     for (int j = 0; j < NQB; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) o[i][j][r] = 0.f;
-  // Scores are in log2 units: the queries arrive scaled by sm_scale*log2(e).
-  // m is each query column's running offset, a value the seed operand holds
-  // exactly.  Every 32-key block's S^T accumulators start from the seed
-  // product, -m for a valid key and -m - 1e30 for a masked one, so
-  // P = exp2(S^T) directly and masked keys get P = 0.  m is raised lazily: a
-  // block is accepted while the sum of each lane's P over it stays <= 2^16
-  // (then no P exceeds 2^16 and nothing can overflow); otherwise (the first
-  // block, or a max that rose by more than 16) the block is redone from its
-  // raw scores, with m raised to the block max where that exceeds m by more
-  // than 8, and O and l rescaled.
-  float m[NQB], l[NQB];
-  typename M::Seed nm[NQB];
+  // Scores S = q'.k' (the rounded rotated query and key, products exact in
+  // float32) become base-2 logits x = S * qk_scale - m in one fused
+  // multiply-add, m being each query column's running offset, and P =
+  // exp2(x).  m is raised lazily: a block is accepted while the sum of each
+  // lane's P over it stays <= 2^16 (then no P exceeds 2^16 and nothing can
+  // overflow); otherwise (the first block, or a max that rose by more than
+  // 16) its raw scores are computed again, m is raised to the block max where
+  // that exceeds m by more than 8, and O and l are rescaled.  Keys past their
+  // gather entry's length start from a score near -1e30 (partial tiles
+  // only): P = 0 whatever m is.  Until a column meets a valid key, m holds
+  // kNoKey: every valid key then overflows the sum check, and the redo sets m.
+  const float qs = a.qk_scale;
+  constexpr float kNoKey = -1e20f;
+  float m[NQB], l[NQB], nm[NQB];  // nm = -m
 #pragma unroll
   for (int qb = 0; qb < NQB; ++qb) {
-    m[qb] = -INFINITY;
+    m[qb] = kNoKey;
+    nm[qb] = -kNoKey;
     l[qb] = 0.f;
-    nm[qb] = M::seed_b(INFINITY, hi);
   }
   constexpr float kMaxBlockSum = 65536.f;
   constexpr float kRaise = 8.f;
 
-  // one 64-key tile from LDS: K at ck, V^T at cv, entry lengths of keys l32
-  // and 32 + l32 in cur_lens
-  auto compute_tile = [&](const T* ck, const T* cv, const int (&cur_lens)[2]) {
-    // seed A operands: key kb*32 + l32 is masked when past its gather
-    // entry's valid length (partial pages)
-    typename M::Seed sa[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      sa[kb] = M::seed_a((kb * 32 + l32) % P >= cur_lens[kb] ? 1.f : 0.f, hi);
-    }
-    // seed of key block kb: offset scores, or raw (offset 0) for a redo
-    auto seed = [&](int kb, bool raw, floatx16 (&init)[NQB]) {
-#pragma unroll
-      for (int qb = 0; qb < NQB; ++qb) init[qb] = M::mma_seed(sa[kb], raw ? M::seed_b(0.f, hi) : nm[qb]);
+  // one 64-key tile from LDS: K at ck, V^T at cv, the lengths of its EPT
+  // gather entries in tl
+  auto compute_tile = [&](const T* ck, const T* cv, const i32x4& tl) {
+    const bool partial = tile_partial<P>(tl);
+    // initial S^T accumulators of key block kb: zero, or in a partial tile
+    // the mask product (key row kb*32 + l32 of lane l32)
+    auto init = [&](int kb) {
+      return partial ? M::mma_seed(M::mask_a(key_masked<P>(tl, kb * 32 + l32), hi), M::mask_b(hi)) : zero16();
     };
-    // S^T of the whole tile (both key blocks): s[kb][qb] holds keys
+    // raw scores S^T of key block kb: s[kb][qb] holds keys
     // kb*32 + 8*(r/4) + 4*hi + r%4 of query column l32
-    auto qk_tile = [&](floatx16 (&s)[2][NQB], bool raw) {
-      seed(0, raw, s[0]);
-      seed(1, raw, s[1]);
+    auto qk_block = [&](int kb, floatx16 (&s)[2][NQB]) {
+      const floatx16 s0 = init(kb);
 #pragma unroll
-      for (int dc = 0; dc < NDC; ++dc)
+      for (int qb = 0; qb < NQB; ++qb) s[kb][qb] = s0;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          Frag kf = read_k(ck, L::KP, kb * 32 + l32, dc, hi);
+      for (int dc = 0; dc < NDC; ++dc) {
+        Frag kf = read_k(ck, L::KP, kb * 32 + l32, dc, hi);
 #pragma unroll
-          for (int qb = 0; qb < NQB; ++qb) s[kb][qb] = M::mma(kf, qf[qb][dc], s[kb][qb]);
-        }
+        for (int qb = 0; qb < NQB; ++qb) s[kb][qb] = M::mma(kf, qf[qb][dc], s[kb][qb]);
+      }
     };
-    // exponentials, packing and this lane's sums of key block kb
+    // logits, exponentials, packing and this lane's sums of key block kb
     auto exp_block = [&](int kb, floatx16 (&s)[2][NQB], Frag (&pf)[2][NCH][NQB], float (&ts)[NQB]) {
 #pragma unroll
       for (int qb = 0; qb < NQB; ++qb) {
         ts[qb] = 0.f;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) s[kb][qb][r] = __builtin_amdgcn_exp2f(s[kb][qb][r]);
+        for (int r = 0; r < 16; ++r) s[kb][qb][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][qb][r], qs, nm[qb]));
 #pragma unroll
         for (int ch = 0; ch < NCH; ++ch) {
           pf[kb][ch][qb] = pack_p(s[kb][qb], ch, T());
@@ -841,35 +848,27 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
       for (int qb = 0; qb < NQB; ++qb) bad = bad || !(ts[qb] <= kMaxBlockSum);
       return !__any(bad);
     };
-    // the redo of key blocks kb0..kb1 from raw scores already in s: m raised
-    // to their max where that exceeds it by more than kRaise (O and l
-    // rescaled), then offset scores and exponentials again
-    auto redo = [&](int kb0, int kb1, floatx16 (&s)[2][NQB], Frag (&pf)[2][NCH][NQB], float (&ts)[NQB]) {
+    // the redo of key block kb from its raw scores (computed again): m raised
+    // to the block max where that exceeds it by more than kRaise (O and l
+    // rescaled), then the exponentials again
+    auto redo = [&](int kb, floatx16 (&s)[2][NQB], Frag (&pf)[2][NCH][NQB], float (&ts)[NQB]) {
+      qk_block(kb, s);
 #pragma unroll
       for (int qb = 0; qb < NQB; ++qb) {
-        float x = s[kb0][qb][0];
+        float x = s[kb][qb][0];
 #pragma unroll
-        for (int kb = kb0; kb <= kb1; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) x = fmaxf(x, s[kb][qb][r]);
-        const float mx = half_swap_max(x);
+        for (int r = 1; r < 16; ++r) x = fmaxf(x, s[kb][qb][r]);
+        const float mx = half_swap_max(x) * qs;  // masked keys sit near -1e30 * qs < kNoKey
         if (mx > m[qb] + kRaise) {
-          const float mn = M::exact(mx);
-          const float alpha = __builtin_amdgcn_exp2f(m[qb] - mn);  // 0 while m = -inf
-          m[qb] = mn;
-          nm[qb] = M::seed_b(-mn, hi);
+          const float alpha = __builtin_amdgcn_exp2f(m[qb] - mx);  // 0 while m = kNoKey
+          m[qb] = mx;
+          nm[qb] = -mx;
           o[0][qb] *= alpha;
           o[1][qb] *= alpha;
           l[qb] *= alpha;
         }
-        // a column with no valid key so far keeps m = -inf: its P is 0
-        const float off = m[qb] == -INFINITY ? 0.f : m[qb];
-#pragma unroll
-        for (int kb = kb0; kb <= kb1; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) s[kb][qb][r] -= off;
       }
-      exp_block(kb0, s, pf, ts);
+      exp_block(kb, s, pf, ts);
     };
     // O^T += V^T P^T over key block kb
     auto pv_block = [&](int kb, const Frag (&pf)[2][NCH][NQB]) {
@@ -892,8 +891,8 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
     if constexpr (sizeof(T) == 2) {
       // Two 32-key blocks in flight: block 0's exponentials run beside block
       // 1's QK MFMAs, block 1's beside block 0's PV MFMAs.  Each block's sums
-      // are checked before its PV; block 0's redo covers both blocks (block
-      // 1's scores carry the old offset), block 1's only itself.
+      // are checked before its PV (block 1's scores are raw until its own
+      // exponentials, so block 0's redo does not touch them).
       Frag kf[2][NDC];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -901,7 +900,9 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
         for (int dc = 0; dc < NDC; ++dc) kf[kb][dc] = read_k(ck, L::KP, kb * 32 + l32, dc, hi);
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        seed(kb, false, s[kb]);
+        const floatx16 s0 = init(kb);
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb) s[kb][qb] = s0;
 #pragma unroll
         for (int dc = 0; dc < NDC; ++dc)
 #pragma unroll
@@ -909,16 +910,13 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
       }
       exp_block(0, s, pf, ts);
       __builtin_amdgcn_sched_group_barrier(0x100, 2 * NDC, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, NQB * (NDC + 2), 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, NQB * NDC, 0);
 #pragma unroll
       for (int i = 0; i < NDC * NQB; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
       }
-      if (!sums_ok(ts)) {
-        qk_tile(s, true);
-        redo(0, 1, s, pf, ts);
-      }
+      if (!sums_ok(ts)) redo(0, s, pf, ts);
 #pragma unroll
       for (int qb = 0; qb < NQB; ++qb) l[qb] += ts[qb];
 
@@ -930,40 +928,22 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
       }
-      if (!sums_ok(ts)) {
-        seed(1, true, s[1]);
-#pragma unroll
-        for (int dc = 0; dc < NDC; ++dc) {
-          const Frag kf1 = read_k(ck, L::KP, 32 + l32, dc, hi);
-#pragma unroll
-          for (int qb = 0; qb < NQB; ++qb) s[1][qb] = M::mma(kf1, qf[qb][dc], s[1][qb]);
-        }
-        redo(1, 1, s, pf, ts);
-      }
+      if (!sums_ok(ts)) redo(1, s, pf, ts);
 #pragma unroll
       for (int qb = 0; qb < NQB; ++qb) l[qb] += ts[qb];
       pv_block(1, pf);
     } else {
-      // fp32: the whole tile at once
-      qk_tile(s, false);
-      float t1s[NQB];
-      exp_block(0, s, pf, ts);
-      exp_block(1, s, pf, t1s);
+      // fp32: block by block
 #pragma unroll
-      for (int qb = 0; qb < NQB; ++qb) ts[qb] += t1s[qb];
-      if (!sums_ok(ts)) {
-        qk_tile(s, true);
-        redo(0, 1, s, pf, ts);
-        exp_block(1, s, pf, t1s);
+      for (int kb = 0; kb < 2; ++kb) {
+        qk_block(kb, s);
+        exp_block(kb, s, pf, ts);
+        if (!sums_ok(ts)) redo(kb, s, pf, ts);
 #pragma unroll
-        for (int qb = 0; qb < NQB; ++qb) ts[qb] += t1s[qb];
+        for (int qb = 0; qb < NQB; ++qb) l[qb] += ts[qb];
+        pv_block(kb, pf);
       }
-#pragma unroll
-      for (int qb = 0; qb < NQB; ++qb) l[qb] += ts[qb];
-      pv_block(0, pf);
-      pv_block(1, pf);
     }
-
   };
 
   const int n = max(t1 - t0, 0);
@@ -981,7 +961,7 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
     DL ld;
     ld.init(h, a.H, tid);
     typename DL::Ids ide, ido;  // ids of the tiles at even / odd distance from t0
-    int lc[2], l1[2], l2[2];    // lengths: this tile, next, next but one
+    i32x4 lc, l1, l2;           // entry lengths: this tile, next, next but one
     const char* kp = (const char*)a.kpool;
     const char* vp = (const char*)a.vpool;
     char* lbase = (char*)&lt[0][0];
@@ -1000,10 +980,10 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
     ready(ido);
     asm volatile("" ::: "memory");
     ld.issue(kp, vp, ide, lbase, wave);
-    DL::lens_of(ide, l32, lc);
+    lc = ide.ln;
     ld.fetch(a, t0 + 2, ide);
     ld.issue(kp, vp, ido, lbase + BB, wave);
-    DL::lens_of(ido, l32, l1);
+    l1 = ido.ln;
     asm volatile("" ::: "memory");
     wait_vmem<DL::NISSUE>();  // tile t0 and the ids of tile t0 + 2 have landed
     asm volatile("" ::: "memory");
@@ -1012,7 +992,7 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
     auto step = [&](int i, typename DL::Ids& fx, const typename DL::Ids& iy) {
       ld.fetch(a, t0 + i + 3, fx);
       ld.issue(kp, vp, iy, lbase + ((i + 2) % 3) * BB, wave);
-      DL::lens_of(iy, l32, l2);
+      l2 = iy.ln;
       asm volatile("" ::: "memory");  // the loads above stay ahead of the count below
       const T* ck = lt[i % 3];
       compute_tile(ck, ck + VOFF, lc);
@@ -1021,10 +1001,8 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
       asm volatile("" ::: "memory");
       __builtin_amdgcn_s_barrier();  // buffer i % 3 is free, tile i + 1 visible to all waves
       asm volatile("" ::: "memory");
-      lc[0] = l1[0];
-      lc[1] = l1[1];
-      l1[0] = l2[0];
-      l1[1] = l2[1];
+      lc = l1;
+      l1 = l2;
     };
     for (int i = 0; i < n; i += 2) {
       step(i, ido, ide);
@@ -1042,7 +1020,7 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
       ld.fetch_pages(a, t0 + 1, tid);
       ld.store(lt[t0 & 1], tid);
     }
-    int cur_lens[2] = {ld.dlens[0], ld.dlens[1]};  // entry lengths of the tile in LDS
+    i32x4 cur_lens = ld.dlen;  // entry lengths of the tile in LDS
     __syncthreads();
     for (int tile = t0; tile < t1; ++tile) {
       const int buf = tile & 1;
@@ -1054,8 +1032,7 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
       compute_tile(lt[buf], lt[buf] + VOFF, cur_lens);
       // the other buffer was last read in the previous tile, before its barrier
       if (more) ld.store(lt[buf ^ 1], tid);
-      cur_lens[0] = ld.dlens[0];
-      cur_lens[1] = ld.dlens[1];
+      cur_lens = ld.dlen;
       __syncthreads();
     }
   }

@@ -97,13 +97,13 @@ struct gca_cache {
   int32_t* compact = nullptr;
   int32_t* sel_page = nullptr;
   int32_t* sel_len = nullptr;
-  float2* rope_t = nullptr;
-  float2* rope_h = nullptr;
-  float2* rope_w = nullptr;
+  double2* rope_t = nullptr;
+  double2* rope_h = nullptr;
+  double2* rope_w = nullptr;
   gca::RopeTabs tabs{};
   float* o_part = nullptr;
   float* lse_part = nullptr;
-  void* qrot = nullptr;  // prepared queries (rotated, scaled) of the current attention call
+  void* qrot = nullptr;  // prepared (rotated) queries of the current attention call
   void* static_scratch = nullptr;  // this device's copy of `scratch` (gca_step_static)
   // tiles of a first-dispatched split per tile of a second-dispatched one
   float split_ratio = 1.7f;
@@ -141,20 +141,20 @@ hipError_t dmalloc(T** p, size_t bytes) {
 
 // Rotary tables for the [t | h | w] split of the head dim: d_h = d_w =
 // 2 * (D / 6), d_t = D - d_h - d_w; pair j of an axis block of width d turns
-// by pos * theta^(-2j/d).  Evaluated in double, stored as float (cos, sin).
-void build_rope(const gca::Geometry& g, std::vector<float2>* t, std::vector<float2>* h,
-                std::vector<float2>* w, int* nt, int* nh, int* nw) {
+// by pos * theta^(-2j/d).  (cos, sin) evaluated and stored in double.
+void build_rope(const gca::Geometry& g, std::vector<double2>* t, std::vector<double2>* h,
+                std::vector<double2>* w, int* nt, int* nh, int* nw) {
   int dh = 2 * (g.D / 6), dw = dh, dt = g.D - dh - dw;
   *nt = dt / 2;
   *nh = dh / 2;
   *nw = dw / 2;
-  auto fill = [&](std::vector<float2>* out, int64_t npos, int width) {
+  auto fill = [&](std::vector<double2>* out, int64_t npos, int width) {
     int npairs = width / 2;
     out->resize((size_t)npos * npairs);
     for (int64_t p = 0; p < npos; ++p)
       for (int j = 0; j < npairs; ++j) {
         double ang = (double)p * std::pow((double)g.theta, -(double)(2 * j) / width);
-        (*out)[(size_t)p * npairs + j] = make_float2((float)std::cos(ang), (float)std::sin(ang));
+        (*out)[(size_t)p * npairs + j] = make_double2(std::cos(ang), std::sin(ang));
       }
   };
   fill(t, g.max_frames, dt);
@@ -259,8 +259,8 @@ gca::EvictArgs evict_args(gca_cache* c, const gca::EvictStep& st) {
   return a;
 }
 
-// The attention's queries: rotated when rope = 1 and scaled by
-// sm_scale * log2(e), rounded once, into the query workspace.
+// The attention's queries: rotated when rope = 1 (rounded once to the cache
+// dtype), else copied, into the query workspace.
 gca::RopeArgs query_args(gca_cache* c, int64_t frame_idx, const void* q, void* dst, int nf = 1) {
   gca::RopeArgs ra;
   ra.x = q;
@@ -270,7 +270,6 @@ gca::RopeArgs query_args(gca_cache* c, int64_t frame_idx, const void* q, void* d
   ra.T = c->g.T;
   ra.H = c->g.H;
   ra.rotate = c->g.rope;
-  ra.scale = (float)((double)c->g.scale * 1.4426950408889634);
   ra.tabs = c->tabs;
   return ra;
 }
@@ -336,6 +335,7 @@ int attend_launch(gca_cache* c, int64_t frame_idx, void* out, float* lse, const 
   const int n_tiles = sp.n_tiles, S = sp.S;
   gca::AttnArgs a;
   a.q = w.qrot;
+  a.qk_scale = (float)((double)g.scale * 1.4426950408889634);
   a.kpool = c->kpool;
   a.vpool = c->vpool;
   a.sel_page = c->sel_page;
@@ -472,19 +472,19 @@ int gca_cache_create(const gca_config* cfg, gca_cache** out) {
   if ((e = hipMemcpy(c->ring, ring.data(), sizeof(int32_t) * g.N, hipMemcpyHostToDevice)) != hipSuccess)
     return fail(e, "upload ring");
   if (g.rope) {
-    std::vector<float2> t, h, w;
+    std::vector<double2> t, h, w;
     int nt, nh, nw;
     build_rope(g, &t, &h, &w, &nt, &nh, &nw);
     // the kernels load the cos/sin of two pairs at once (12, 10, 10 pairs for D = 64)
     if ((nt | nh | nw) & 1) return fail(hipErrorInvalidValue, "rotary split with an odd pair count");
-    if ((e = dmalloc(&c->rope_t, sizeof(float2) * t.size())) != hipSuccess) return fail(e, "hipMalloc rope");
-    if ((e = dmalloc(&c->rope_h, sizeof(float2) * h.size())) != hipSuccess) return fail(e, "hipMalloc rope");
-    if ((e = dmalloc(&c->rope_w, sizeof(float2) * w.size())) != hipSuccess) return fail(e, "hipMalloc rope");
-    if ((e = hipMemcpy(c->rope_t, t.data(), sizeof(float2) * t.size(), hipMemcpyHostToDevice)) != hipSuccess)
+    if ((e = dmalloc(&c->rope_t, sizeof(double2) * t.size())) != hipSuccess) return fail(e, "hipMalloc rope");
+    if ((e = dmalloc(&c->rope_h, sizeof(double2) * h.size())) != hipSuccess) return fail(e, "hipMalloc rope");
+    if ((e = dmalloc(&c->rope_w, sizeof(double2) * w.size())) != hipSuccess) return fail(e, "hipMalloc rope");
+    if ((e = hipMemcpy(c->rope_t, t.data(), sizeof(double2) * t.size(), hipMemcpyHostToDevice)) != hipSuccess)
       return fail(e, "upload rope");
-    if ((e = hipMemcpy(c->rope_h, h.data(), sizeof(float2) * h.size(), hipMemcpyHostToDevice)) != hipSuccess)
+    if ((e = hipMemcpy(c->rope_h, h.data(), sizeof(double2) * h.size(), hipMemcpyHostToDevice)) != hipSuccess)
       return fail(e, "upload rope");
-    if ((e = hipMemcpy(c->rope_w, w.data(), sizeof(float2) * w.size(), hipMemcpyHostToDevice)) != hipSuccess)
+    if ((e = hipMemcpy(c->rope_w, w.data(), sizeof(double2) * w.size(), hipMemcpyHostToDevice)) != hipSuccess)
       return fail(e, "upload rope");
     c->tabs.t = c->rope_t;
     c->tabs.h = c->rope_h;
@@ -765,7 +765,6 @@ int gca_rope3d(gca_cache* c, int64_t frame_idx, const void* x, void* y, gca_stre
   a.T = c->g.T;
   a.H = c->g.H;
   a.rotate = 1;
-  a.scale = 1.f;
   a.tabs = c->tabs;
   Prof p(c, 5, s);
   GCA_HIP(gca::launch_rope(c->g.dtype, a, s), "rope kernel launch");

@@ -130,6 +130,19 @@ class FrameStream:
                 self._drift_cache[f] = (mk, mv)
         return mk, mv
 
+    def prefetch_drift(self, n_frames: int) -> None:
+        """Walk the drift through frames 0 .. n_frames - 1 once and keep every
+        frame's offsets, so later kv() calls only read (and may run in threads)."""
+        mk, mv = self._drift_cache[0]
+        for f in range(1, n_frames):
+            if f in self._drift_cache:
+                mk, mv = self._drift_cache[f]
+                continue
+            z = normals(self.seed, f, TENSOR_DRIFT, 2 * self.H * self.D).reshape(2, self.H, self.D)
+            mk = mk + self.drift_sigma * z[0]
+            mv = mv + self.drift_sigma * z[1]
+            self._drift_cache[f] = (mk, mv)
+
     def q(self, frame: int) -> np.ndarray:
         return to_dtype(self.base(frame, TENSOR_Q), self.dtype)
 

@@ -1,9 +1,9 @@
 """GPU parity of the HIP path against the CPU oracle, through the C ABI.
 
-Bar: page tables, ring and gather lists bit-exact; V pages bit-exact and K'
-pages within one unit in the last place (the library rotates in float32 from
-float32 tables, the oracle in float64); attention max abs error <= 1e-5 for the
-float32 stream and <= 2e-2 for bf16 streams.
+Bar: page tables, ring and gather lists bit-exact; K' and V pages bit-exact
+(the library rotates in float64 with the oracle's operations and rounds once,
+as the oracle does); attention max abs error <= 1e-5 for the float32 stream
+and <= 2e-2 for bf16 streams; LSE within the derived P-rounding budget.
 """
 from __future__ import annotations
 
@@ -19,44 +19,15 @@ from tests.gpu_pair import Pair, dev, gca, oracle_cfg, stream_of
 pytestmark = pytest.mark.gpu
 
 TOL = {"f32": 1e-5, "bf16": 2e-2}
-# LSE bar beside the exact query-rounding shift below: the library's row sum
-# adds the probabilities P as rounded to the storage type for the P.V product,
-# each within a relative 2^-8 (bf16 unit roundoff) of its exact value, so the
-# log of the sum moves by at most ln(1 + 2^-8) < 2^-8 (a worst case met only
-# when few keys carry the weight); 1e-5 covers the float32 accumulation, the
-# exp2 and the log.
+# LSE bar: the library rounds the rotated query q' to the storage type as the
+# oracle does and scales the scores by float32(sm_scale * log2 e) after the
+# dot product, so its logits are the oracle's up to float32 accumulation.  Its
+# row sum adds the probabilities P as rounded to the storage type for the P.V
+# product, each within a relative 2^-8 (bf16 unit roundoff) of its exact
+# value, so the log of the sum moves by at most ln(1 + 2^-8) < 2^-8 (a worst
+# case met only when few keys carry the weight); 1e-5 covers the float32
+# accumulation, the exp2 and the log.
 LSE_TOL = {"f32": 1e-5, "bf16": 2.0 ** -8 + 1e-5}
-
-
-def query_rounding_shift(pair, f, q, rows):
-    """Exact LSE difference (float64) between the two rounding points of the
-    query operand, per (row, head) of `rows`.  The oracle rounds the rotated
-    query q' to the storage type and takes logits sm_scale * q'.k; the library
-    multiplies the float32 rotation by s = float32(sm_scale * log2(e)), rounds
-    once to the storage type and takes base-2 logits, i.e. natural logits
-    ln(2) * round(q' s).k.  Both LSEs are evaluated here in float64 over the
-    oracle's own context (stored K') from the oracle's float64 rotation."""
-    from paged_kv_cache_gca_amd.synth import round_bf16
-    cfg = pair.orc.cfg
-    k = pair.orc.context()[0].astype(np.float64)                       # (n, H, D)
-    qr = oracle.rope(cfg, f, q) if cfg.rope else q.astype(np.float64)  # (T, H, D)
-    q32 = qr[rows].astype(np.float32)
-    scale = cfg.sm_scale if cfg.sm_scale is not None else cfg.D ** -0.5
-    s32 = np.float32(scale * 1.4426950408889634)
-    if pair.w.dtype == "bf16":
-        q_orc, q_lib = round_bf16(q32), round_bf16(q32 * s32)
-    else:
-        q_orc, q_lib = q32, q32 * s32
-    q_orc = q_orc.astype(np.float64) * scale
-    q_lib = q_lib.astype(np.float64) * np.log(2.0)
-
-    def lse(qq, kk):
-        z = qq @ kk.T                                                   # (R, n)
-        m = z.max(axis=1, keepdims=True)
-        return (m + np.log(np.exp(z - m).sum(axis=1, keepdims=True)))[:, 0]
-
-    return np.stack([lse(q_lib[:, h], k[:, h]) - lse(q_orc[:, h], k[:, h]) for h in range(k.shape[1])],
-                    axis=1)
 
 
 def _cmp_attention(pair, f, rows=None):
@@ -78,13 +49,10 @@ def _cmp_outputs(pair, f, q, out, lse, rows=None):
         tol = max(tol, 2e-2)
     assert np.isfinite(o).all()
     assert err <= tol, (f, err)
-    # the LSE bar: the derived budget for P rounding and accumulation, plus the
-    # exact shift from the query operand's rounding point (an empty row has
-    # lse = -inf on both sides)
+    # the LSE bar (an empty row has lse = -inf on both sides)
     fin = np.isfinite(lse_ref)
     assert (l[~fin] == lse_ref[~fin]).all()
-    bound = LSE_TOL[pair.w.dtype] + np.abs(query_rounding_shift(pair, f, q, rows))
-    assert (ldiff[fin] <= bound[fin]).all(), (f, lerr, float(bound[fin].max()))
+    assert (ldiff[fin] <= LSE_TOL[pair.w.dtype]).all(), (f, lerr)
     return err, lerr
 
 
@@ -96,8 +64,7 @@ def test_tiny_f32_stream_full_parity():
     for f in range(w.n_frames):
         p.step(f)
         gs = p.check_state()
-        mis, tot = p.check_pages(gs, k_ulps=0)
-        assert mis == 0
+        p.check_pages(gs)
         errs.append(_cmp_attention(p, f))
     print("tiny f32 max err", max(e[0] for e in errs))
 
@@ -113,18 +80,14 @@ def test_small_bf16_stream_parity(P, interval, out_dtype):
     """Ragged query tile (300 = 256 + 44), ragged frame tail, TEMP frames."""
     w = WL.Workload(f"small_P{P}", P=P, keyframe_interval=interval, **SMALL)
     p = Pair(w, out_dtype=out_dtype)
-    kmis = ktot = 0
     for f in range(w.n_frames):
         key = p.step(f)
         gs = p.check_state()
-        m, t = p.check_pages(gs)
-        kmis += m
-        ktot += t
+        p.check_pages(gs)
         _cmp_attention(p, f)
         if not key:
             p.rollback(f)
             p.check_state()
-    assert kmis <= 1e-3 * ktot, (kmis, ktot)
 
 
 @pytest.mark.parametrize("H,T,ns,gh,gw", [(8, 300, 3, 9, 33), (12, 300, 3, 9, 33), (8, 1004, 5, 27, 37)])
@@ -272,6 +235,57 @@ def test_long_stream_prefix_sampled(w, last, samples):
             p.rollback(f)
 
 
+@pytest.mark.parametrize("w,tail", [
+    (WL.STREAM1000_W64, (997, 998, 999)),
+    (WL.STREAM10K_KF4, (9996, 9997, 9998, 9999)),
+])
+def test_long_stream_end_sampled(w, tail):
+    """The whole stream on the GPU through gca_step (the bench's launch
+    sequence); attention on sampled rows against the oracle at its last frames:
+    the 1,000-frame stream at n_ctx 77,415, the 10,000-frame drifting stream at
+    its last keyframe (trajectory 32,071 tokens, |K|, |V| grown to about 10 by
+    the walk) and the three non-keyframes after it.  The oracle is fed every
+    keyframe (non-keyframes before the tail leave no trace, as the rollback
+    pins show); page tables and gather lists are compared at the tail too."""
+    from tests.gpu_pair import DeviceFrames, host_frames
+    p = Pair(w, data=False)
+    p.orc = oracle.OracleCache(oracle_cfg(w))          # a data-carrying oracle
+    dfr = DeviceFrames(w, p.fs, check=(0, 1, tail[0]))
+    rows = _rows(w.T, seed=5)
+    t0 = tail[0]
+    out = torch.empty((w.T, w.H, w.D), dtype=torch.float32, device="cuda")
+    lse = torch.empty((w.T, w.H), dtype=torch.float32, device="cuda")
+    for f in range(t0):
+        kd, vd = dfr.kv(f)
+        assert p.gpu.step(f, kd, vd, dfr.q[f % dfr.n], out, lse, keyframe=w.is_keyframe(f)) == 0
+    for f, k, v in host_frames(p.fs, [f for f in range(t0) if w.is_keyframe(f)]):
+        assert p.orc.append(f, k, v) == 0 and p.orc.evict() == 0
+    torch.cuda.synchronize()
+    for f in tail:
+        key = w.is_keyframe(f)
+        k, v = p.fs.kv(f)
+        q = p.fs.q(f)
+        kd, vd = dfr.kv(f)
+        assert p.gpu.step(f, kd, vd, dev(q, w.dtype), out, lse, keyframe=key) == 0
+        assert p.orc.append(f, k, v, temp=not key) == 0
+        if key:
+            assert p.orc.evict() == 0
+        if key:  # the gather list of the step (a non-keyframe's is gone with its rollback)
+            st = p.gpu.export_state()
+            page, ln, n_ctx = p.orc.select()
+            np.testing.assert_array_equal(st["sel_page"], page)
+            np.testing.assert_array_equal(st["sel_len"], ln)
+            assert st["n_ctx"] == n_ctx
+        _cmp_outputs(p, f, q, out, lse, rows)
+        if not key:
+            assert p.orc.rollback(f) == 0
+    p.check_state()
+    if w is WL.STREAM10K_KF4:
+        assert p.orc.state()["traj_len"] == 32071
+        kc, vc = p.orc.context()[:2]
+        assert np.abs(kc).max() > 8.0 and np.abs(vc).max() > 8.0   # the drifted values the test is about
+
+
 def test_ring20k_tail_sampled():
     """Strict 12-frame window at the end of the 20,000-frame stream (t near 19,999)."""
     w = WL.RING20K_W12
@@ -326,9 +340,7 @@ def test_rope_standalone_matches_oracle():
         ref64 = oracle.rope(oracle_cfg(w, max_frames=20000), f, x)
         m, e = np.frexp(ref64)
         ref = np.ldexp(np.rint(m * 256.0), e - 8)
-        diff = got != ref
-        assert (np.abs(got - ref)[diff] <= np.abs(ref[diff]) * 2.0 ** -7).all()
-        assert diff.mean() < 1e-3, diff.mean()
+        np.testing.assert_array_equal(got, ref)   # bit for bit: float64 rotation, one rounding
 
 
 def test_fused_rope_in_append_is_bitwise_standalone():
@@ -434,8 +446,7 @@ def test_lazy_rescale_paths(dtype):
         else:
             np.testing.assert_allclose(o, 1.0, atol=1e-6)
         l = lse.cpu().numpy().astype(np.float64)
-        bound = LSE_TOL[dtype] + np.abs(query_rounding_shift(p, f, q, np.arange(w.T)))
-        assert (np.abs(l - lse_ref) <= bound).all(), (f, np.abs(l - lse_ref).max())
+        assert (np.abs(l - lse_ref) <= LSE_TOL[dtype]).all(), (f, np.abs(l - lse_ref).max())
         if f == w.n_frames - 1:
             # the data does what the test is about: in context order, some 64-key
             # tile's max logit exceeds every earlier tile's by more than 16 (base 2)
@@ -618,8 +629,7 @@ def test_scale_frames_joint_attention_parity(T, H, P, dtype, A, nf, rope, ns, gh
         assert np.isfinite(o).all()
         err = float(np.abs(o - o_ref[i]).max())
         assert err <= tol, (i, err)
-        bound = LSE_TOL[dtype] + np.abs(query_rounding_shift(p, first + i, q[i], rows))
-        assert (np.abs(l - lse_ref[i]) <= bound).all(), i
+        assert (np.abs(l - lse_ref[i]) <= LSE_TOL[dtype]).all(), i
     p.check_state()
     if not sampled:
         for f in range(A, A + 2):
