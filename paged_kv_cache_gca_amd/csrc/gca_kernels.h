@@ -13,19 +13,19 @@ constexpr int kWaves = 4;       // waves per attention workgroup
 // queries per attention workgroup: 4 waves x 64 (bf16) or x 32 (float32)
 inline int queries_per_wg(int dtype) { return kWaves * (dtype ? 64 : 32); }
 constexpr int kNumXcd = 8;      // MI355X: 8 accelerator complex dies, round-robin dispatch
-// The gather list is written out to (ceil(n_sel / EPT) + 2) * EPT entries, EPT =
+// The gather list is written out to (ceil(n_sel / EPT) + 4) * EPT entries, EPT =
 // kKeysPerTile / P entries per tile: entries past n_sel name the zero page (page
 // N, never handed out) with length 0, so the attention loader can fetch page ids
-// two tiles ahead unchecked.
+// up to four tiles ahead unchecked.
 //
 // Pool invariant: every slot of a live page past its entry's valid length holds
 // zeros (append zeroes the frame's last page past T, evict zeroes the last
 // trajectory page past the tokens it wrote).  Masked keys get P = 0 and meet a
 // zero V row, so stale non-finite data can never reach an output.
-constexpr int kSelPad = 3 * (kKeysPerTile / 16);
+constexpr int kSelPad = 5 * (kKeysPerTile / 16);
 inline int padded_sel(int n_sel, int P) {
   int ept = kKeysPerTile / P;
-  return ((n_sel + ept - 1) / ept + 2) * ept;
+  return ((n_sel + ept - 1) / ept + 4) * ept;
 }
 
 // Rotary tables: (cos, sin) in float64, evaluated on the host.

@@ -507,7 +507,14 @@ __device__ inline i32x4 load_lens(const int32_t* p) {
   return v;
 }
 
-__device__ inline int pick(i32x4 v, int j) { return j == 0 ? v.x : j == 1 ? v.y : j == 2 ? v.z : v.w; }
+// element j of v (a per-lane index): straight-line selects, no divergent branches
+__device__ inline int pick(i32x4 v, int j) {
+  int r = v.x;
+  r = j == 1 ? v.y : r;
+  r = j == 2 ? v.z : r;
+  r = j == 3 ? v.w : r;
+  return r;
+}
 
 // Key `key` of a tile is masked when its slot lies past its gather entry's
 // valid length (a partial page, or padding).
@@ -630,45 +637,52 @@ struct DmaLoader {
   struct Ids {
     i32x4 pg, ln;
   };
-  uint32_t koff[2], voff[2];  // piece offsets inside a (page, head) block (bytes)
-  int kent[2], vent[2];       // their gather entries within a tile
   uint32_t page_bytes, head_off;
+  int w, lane;
 
   __device__ void init(int h, int H, int tid) {
-    const int w = tid >> 6, lane = tid & 63;
+    w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: the LDS destinations need no waterfall
+    lane = tid & 63;
     page_bytes = (uint32_t)(H * P * kHeadDim * 2);
     head_off = (uint32_t)(h * P * kHeadDim * 2);
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int pos = (w * 2 + j) * 64 + lane;        // 16-byte position in the K tile
-      const int r = pos >> 3, c = (pos & 7) ^ ((r >> 1) & 7);  // key row, logical chunk (swz)
-      kent[j] = r / P;
-      koff[j] = (uint32_t)(((r % P) * kHeadDim + c * 8) * 2);
-    }
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int pos = (w * 2 + j) * 64 + lane;        // 16-byte position in the V^T tile
-      const int d = pos >> 3, c = (pos & 7) ^ ((d >> 1) & 7);  // dim row, chunk (8 stored slots)
-      vent[j] = (8 * c) / P;
-      voff[j] = (uint32_t)((d * P + (8 * c) % P) * 2);
-    }
+  }
+  // piece j of this lane in the K tile: its gather entry and its byte offset
+  // inside a (page, head) block (key row r, logical chunk c of the swizzle)
+  __device__ void kpiece(int j, int& ent, uint32_t& off) const {
+    const int pos = (w * 2 + j) * 64 + lane;
+    const int r = pos >> 3, c = (pos & 7) ^ ((r >> 1) & 7);
+    ent = r / P;
+    off = (uint32_t)(((r % P) * kHeadDim + c * 8) * 2);
+  }
+  // piece j in the V^T tile: dim row d, chunk c of 8 stored slots
+  __device__ void vpiece(int j, int& ent, uint32_t& off) const {
+    const int pos = (w * 2 + j) * 64 + lane;
+    const int d = pos >> 3, c = (pos & 7) ^ ((d >> 1) & 7);
+    ent = (8 * c) / P;
+    off = (uint32_t)((d * P + (8 * c) % P) * 2);
   }
   __device__ void fetch(const AttnArgs& a, int tile, Ids& x) const {
     x.pg = load_lens<EPT>(a.sel_page + tile * EPT);
     x.ln = load_lens<EPT>(a.sel_len + tile * EPT);
   }
-  __device__ void issue(const char* kpool, const char* vpool, const Ids& x, char* buf, int w) const {
+  __device__ void issue(const char* kpool, const char* vpool, const Ids& x, char* buf, int /*wave*/) const {
     typedef __attribute__((address_space(3))) void lds_t;
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
-      __builtin_amdgcn_global_load_lds(kpool + (uint64_t)(uint32_t)pick(x.pg, kent[j]) * page_bytes + head_off +
-                                           koff[j],
+    for (int j = 0; j < 2; ++j) {
+      int ent;
+      uint32_t off;
+      kpiece(j, ent, off);
+      __builtin_amdgcn_global_load_lds(kpool + (uint64_t)(uint32_t)pick(x.pg, ent) * page_bytes + head_off + off,
                                        (lds_t*)(buf + (w * 2 + j) * 1024), 16, 0, 0);
+    }
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
-      __builtin_amdgcn_global_load_lds(vpool + (uint64_t)(uint32_t)pick(x.pg, vent[j]) * page_bytes + head_off +
-                                           voff[j],
+    for (int j = 0; j < 2; ++j) {
+      int ent;
+      uint32_t off;
+      vpiece(j, ent, off);
+      __builtin_amdgcn_global_load_lds(vpool + (uint64_t)(uint32_t)pick(x.pg, ent) * page_bytes + head_off + off,
                                        (lds_t*)(buf + KBYTES + (w * 2 + j) * 1024), 16, 0, 0);
+    }
   }
 };
 
@@ -705,46 +719,28 @@ __device__ inline float half_swap_max(float x) {
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
-template <typename T, int P>
-__global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
-  using M = Mfma<T>;
-  using Frag = typename M::Frag;
-  using L = TileLoader<T, P>;   // fp32: through registers, two buffers
-  using DL = DmaLoader<P>;      // bf16: straight into LDS, three buffers
-  // bf16 tiles: straight into LDS at P = 64, through registers at P = 16/32
-  // (measured faster each way)
-  constexpr bool DMA = sizeof(T) == 2 && P == 64;
-  constexpr int NQB = M::NQB;
-  constexpr int KPL = M::KPL;
-  constexpr int NDC = kHeadDim / (2 * KPL);  // MFMAs along the head dim
-  constexpr int NCH = 16 / KPL;              // P^T operands per 32-key block
-  constexpr int QPW = NQB * 32;              // queries per wave
-  constexpr int NBUF = DMA ? 3 : 2;
-  constexpr int BUF_ELEMS = DMA ? DL::BUF_BYTES / (int)sizeof(T) : L::TILE_ELEMS;
-  constexpr int VOFF = DMA ? kKeysPerTile * kHeadDim : kKeysPerTile * L::KP;  // V^T within a buffer
-  __shared__ __attribute__((aligned(16))) T lt[NBUF][BUF_ELEMS];
-
-  // workgroup -> (head, split, q tile).  Dispatch is round-robin over the
-  // XCDs, each with its own L2.  With H a multiple of 8, all workgroups of a
-  // head run on one XCD (XCD = h % 8), so both its K/V pages and each q
-  // tile's queries come from HBM once and are shared through that L2; the q
-  // tiles of one split are dispatched consecutively.  Otherwise the q tiles
-  // of one (head, split) share an XCD.
-  //
-  // Split sizes (head-major, S even): the even splits of every (head, q tile)
-  // are dispatched first, as the first workgroup of their CU, and hold
-  // t_even tiles; the odd ones come second and hold t_odd.  Two workgroups
-  // share a CU and the first one dispatched issues ahead of the other, so
-  // uneven splits let both finish together.  Boundaries depend only on the
-  // launch parameters: results stay deterministic.
+// Workgroup -> (head, split, q tile) and its tile range [t0, t1); false for a
+// workgroup past the work.  Dispatch is round-robin over the XCDs, each with
+// its own L2.  With H a multiple of 8, all workgroups of a head run on one XCD
+// (XCD = h % 8), so both its K/V pages and each q tile's queries come from HBM
+// once and are shared through that L2; the q tiles of one split are
+// dispatched consecutively.  Otherwise the q tiles of one (head, split) share
+// an XCD.
+//
+// Split sizes (head-major, S even): the even splits of every (head, q tile)
+// are dispatched first, as the first workgroup of their CU, and hold
+// tiles_per_split tiles; the odd ones come second and hold t_odd.  Two
+// workgroups share a CU and the first one dispatched issues ahead of the
+// other, so uneven splits let both finish together.  Boundaries depend only
+// on the launch parameters: results stay deterministic.
+__device__ inline bool attn_place(const AttnArgs& a, int& h, int& split, int& qt, int& t0, int& t1) {
   const int b = blockIdx.x;
   const int xcd = b % kNumXcd, kx = b / kNumXcd;
-  int h, split, qt;
   if (a.head_major) {
-    const int per = a.S * a.n_qtiles;           // workgroups of one head
+    const int per = a.S * a.n_qtiles;              // workgroups of one head
     const int nh = (a.H + kNumXcd - 1) / kNumXcd;  // heads on this XCD
     if (a.t_odd > 0) {
-      const int halfw = nh * per / 2;             // even (then odd) splits of all those heads
+      const int halfw = nh * per / 2;              // even (then odd) splits of all those heads
       const int odd = kx / halfw, r = kx % halfw, j = r % (per / 2);
       h = xcd + kNumXcd * (r / (per / 2));
       split = 2 * (j / a.n_qtiles) + odd;
@@ -755,365 +751,227 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
       split = j / a.n_qtiles;
       qt = j % a.n_qtiles;
     }
-    if (h >= a.H) return;
+    if (h >= a.H) return false;
   } else {
     const int unit = (kx / a.n_qtiles) * kNumXcd + xcd;
-    if (unit >= a.n_units) return;
+    if (unit >= a.n_units) return false;
     qt = kx % a.n_qtiles;
     h = unit / a.S;
     split = unit % a.S;
   }
+  t0 = a.t_odd > 0 ? (split >> 1) * (a.tiles_per_split + a.t_odd) + (split & 1) * a.tiles_per_split
+                   : split * a.tiles_per_split;
+  t1 = min(a.n_tiles, t0 + ((split & 1) && a.t_odd > 0 ? a.t_odd : a.tiles_per_split));
+  return true;
+}
+
+// float32 paged attention (the float32 cache): 4 waves x 32 queries of one
+// head per workgroup, over one split of the gather list.  Per 64-key tile, K
+// (64 keys x 64 dims) and V^T (64 dims x 64 keys) are staged in LDS (two
+// buffers, each thread's next chunks held in registers), then each wave
+// computes S^T = K Q^T with 32x32x2 MFMAs, one query column per lane, and
+// O^T += V^T P^T from the S^T accumulators.  Scores, lazy offsets and masks as
+// described in k_attn_bf.
+template <int P>
+__global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
+  using M = Mfma<float>;
+  using Frag = float;
+  using L = TileLoader<float, P>;
+  constexpr int NDC = kHeadDim / 2;  // MFMAs along the head dim
+  constexpr int NCH = 16;            // P^T operands per 32-key block
+  constexpr int QPW = 32;            // queries per wave
+  constexpr int VOFF = kKeysPerTile * L::KP;  // V^T within a buffer
+  __shared__ __attribute__((aligned(16))) float lt[2][L::TILE_ELEMS];
+
+  int h, split, qt, t0, t1;
+  if (!attn_place(a, h, split, qt, t0, t1)) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hi = lane >> 5;
-  const int t0 = a.t_odd > 0 ? (split >> 1) * (a.tiles_per_split + a.t_odd) + (split & 1) * a.tiles_per_split
-                             : split * a.tiles_per_split;
-  const int t1 = min(a.n_tiles, t0 + ((split & 1) && a.t_odd > 0 ? a.t_odd : a.tiles_per_split));
   const int qbase = (qt * kWaves + wave) * QPW;
-  const T* kpool = (const T*)a.kpool;
-  const T* vpool = (const T*)a.vpool;
 
-  // the wave's query fragments stay in registers (B operands)
-  Frag qf[NQB][NDC];
+  Frag qf[1][NDC];
   load_q(a, qbase, h, l32, hi, qf);
-
-  floatx16 o[2][NQB];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < NQB; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[i][j][r] = 0.f;
-  // Scores S = q'.k' (the rounded rotated query and key, products exact in
-  // float32) become base-2 logits x = S * qk_scale - m in one fused
-  // multiply-add, m being each query column's running offset, and P =
-  // exp2(x).  m is raised lazily: a block is accepted while the sum of each
-  // lane's P over it stays <= 2^16 (then no P exceeds 2^16 and nothing can
-  // overflow); otherwise (the first block, or a max that rose by more than
-  // 16) its raw scores are computed again, m is raised to the block max where
-  // that exceeds m by more than 8, and O and l are rescaled.  Keys past their
-  // gather entry's length start from a score near -1e30 (partial tiles
-  // only): P = 0 whatever m is.  Until a column meets a valid key, m holds
-  // kNoKey: every valid key then overflows the sum check, and the redo sets m.
+  floatx16 o[2] = {zero16(), zero16()};
   const float qs = a.qk_scale;
   constexpr float kNoKey = -1e20f;
-  float m[NQB], l[NQB], nm[NQB];  // nm = -m
-#pragma unroll
-  for (int qb = 0; qb < NQB; ++qb) {
-    m[qb] = kNoKey;
-    nm[qb] = -kNoKey;
-    l[qb] = 0.f;
-  }
   constexpr float kMaxBlockSum = 65536.f;
   constexpr float kRaise = 8.f;
+  float m = kNoKey, nm = -kNoKey, l = 0.f;
 
-  // one 64-key tile from LDS: K at ck, V^T at cv, the lengths of its EPT
-  // gather entries in tl
-  auto compute_tile = [&](const T* ck, const T* cv, const i32x4& tl) {
+  // one 32-key block kb of the tile in LDS: K at ck, V^T at cv, entry lengths tl
+  auto block = [&](const float* ck, const float* cv, const i32x4& tl, int kb) {
     const bool partial = tile_partial<P>(tl);
-    // initial S^T accumulators of key block kb: zero, or in a partial tile
-    // the mask product (key row kb*32 + l32 of lane l32)
-    auto init = [&](int kb) {
-      return partial ? M::mma_seed(M::mask_a(key_masked<P>(tl, kb * 32 + l32), hi), M::mask_b(hi)) : zero16();
+    auto qk = [&]() {
+      floatx16 s = partial ? M::mma_seed(M::mask_a(key_masked<P>(tl, kb * 32 + l32), hi), M::mask_b(hi))
+                           : zero16();
+#pragma unroll
+      for (int dc = 0; dc < NDC; ++dc) s = M::mma(read_k(ck, L::KP, kb * 32 + l32, dc, hi), qf[0][dc], s);
+      return s;
     };
-    // raw scores S^T of key block kb: s[kb][qb] holds keys
-    // kb*32 + 8*(r/4) + 4*hi + r%4 of query column l32
-    auto qk_block = [&](int kb, floatx16 (&s)[2][NQB]) {
-      const floatx16 s0 = init(kb);
+    auto expo = [&](floatx16& s) {
+      float ts = 0.f;
 #pragma unroll
-      for (int qb = 0; qb < NQB; ++qb) s[kb][qb] = s0;
-#pragma unroll
-      for (int dc = 0; dc < NDC; ++dc) {
-        Frag kf = read_k(ck, L::KP, kb * 32 + l32, dc, hi);
-#pragma unroll
-        for (int qb = 0; qb < NQB; ++qb) s[kb][qb] = M::mma(kf, qf[qb][dc], s[kb][qb]);
+      for (int r = 0; r < 16; ++r) {
+        s[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], qs, nm));
+        ts += s[r];
       }
+      return ts;
     };
-    // logits, exponentials, packing and this lane's sums of key block kb
-    auto exp_block = [&](int kb, floatx16 (&s)[2][NQB], Frag (&pf)[2][NCH][NQB], float (&ts)[NQB]) {
+    floatx16 s = qk();
+    float ts = expo(s);
+    if (__any(!(ts <= kMaxBlockSum))) {
+      s = qk();
+      float x = s[0];
 #pragma unroll
-      for (int qb = 0; qb < NQB; ++qb) {
-        ts[qb] = 0.f;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[kb][qb][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][qb][r], qs, nm[qb]));
-#pragma unroll
-        for (int ch = 0; ch < NCH; ++ch) {
-          pf[kb][ch][qb] = pack_p(s[kb][qb], ch, T());
-          ts[qb] = rowsum_add(ts[qb], pf[kb][ch][qb]);
-        }
+      for (int r = 1; r < 16; ++r) x = fmaxf(x, s[r]);
+      const float mx = half_swap_max(x) * qs;
+      if (mx > m + kRaise) {
+        const float alpha = __builtin_amdgcn_exp2f(m - mx);
+        m = mx;
+        nm = -mx;
+        o[0] *= alpha;
+        o[1] *= alpha;
+        l *= alpha;
       }
-    };
-    auto sums_ok = [&](const float (&ts)[NQB]) {
-      bool bad = false;
-#pragma unroll
-      for (int qb = 0; qb < NQB; ++qb) bad = bad || !(ts[qb] <= kMaxBlockSum);
-      return !__any(bad);
-    };
-    // the redo of key block kb from its raw scores (computed again): m raised
-    // to the block max where that exceeds it by more than kRaise (O and l
-    // rescaled), then the exponentials again
-    auto redo = [&](int kb, floatx16 (&s)[2][NQB], Frag (&pf)[2][NCH][NQB], float (&ts)[NQB]) {
-      qk_block(kb, s);
-#pragma unroll
-      for (int qb = 0; qb < NQB; ++qb) {
-        float x = s[kb][qb][0];
-#pragma unroll
-        for (int r = 1; r < 16; ++r) x = fmaxf(x, s[kb][qb][r]);
-        const float mx = half_swap_max(x) * qs;  // masked keys sit near -1e30 * qs < kNoKey
-        if (mx > m[qb] + kRaise) {
-          const float alpha = __builtin_amdgcn_exp2f(m[qb] - mx);  // 0 while m = kNoKey
-          m[qb] = mx;
-          nm[qb] = -mx;
-          o[0][qb] *= alpha;
-          o[1][qb] *= alpha;
-          l[qb] *= alpha;
-        }
-      }
-      exp_block(kb, s, pf, ts);
-    };
-    // O^T += V^T P^T over key block kb
-    auto pv_block = [&](int kb, const Frag (&pf)[2][NCH][NQB]) {
-      Frag vf[NCH][2];
-#pragma unroll
-      for (int ch = 0; ch < NCH; ++ch)
-#pragma unroll
-        for (int db = 0; db < 2; ++db) vf[ch][db] = read_v(cv, L::VP, db * 32 + l32, kb, ch, hi);
-#pragma unroll
-      for (int ch = 0; ch < NCH; ++ch)
-#pragma unroll
-        for (int db = 0; db < 2; ++db)
-#pragma unroll
-          for (int qb = 0; qb < NQB; ++qb) o[db][qb] = M::mma(vf[ch][db], pf[kb][ch][qb], o[db][qb]);
-    };
-
-    floatx16 s[2][NQB];
-    Frag pf[2][NCH][NQB];
-    float ts[NQB];
-    if constexpr (sizeof(T) == 2) {
-      // Two 32-key blocks in flight: block 0's exponentials run beside block
-      // 1's QK MFMAs, block 1's beside block 0's PV MFMAs.  Each block's sums
-      // are checked before its PV (block 1's scores are raw until its own
-      // exponentials, so block 0's redo does not touch them).
-      Frag kf[2][NDC];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int dc = 0; dc < NDC; ++dc) kf[kb][dc] = read_k(ck, L::KP, kb * 32 + l32, dc, hi);
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const floatx16 s0 = init(kb);
-#pragma unroll
-        for (int qb = 0; qb < NQB; ++qb) s[kb][qb] = s0;
-#pragma unroll
-        for (int dc = 0; dc < NDC; ++dc)
-#pragma unroll
-          for (int qb = 0; qb < NQB; ++qb) s[kb][qb] = M::mma(kf[kb][dc], qf[qb][dc], s[kb][qb]);
-      }
-      exp_block(0, s, pf, ts);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2 * NDC, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, NQB * NDC, 0);
-#pragma unroll
-      for (int i = 0; i < NDC * NQB; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
-      }
-      if (!sums_ok(ts)) redo(0, s, pf, ts);
-#pragma unroll
-      for (int qb = 0; qb < NQB; ++qb) l[qb] += ts[qb];
-
-      pv_block(0, pf);
-      exp_block(1, s, pf, ts);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2 * NCH, 0);
-#pragma unroll
-      for (int i = 0; i < 2 * NCH * NQB; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
-      }
-      if (!sums_ok(ts)) redo(1, s, pf, ts);
-#pragma unroll
-      for (int qb = 0; qb < NQB; ++qb) l[qb] += ts[qb];
-      pv_block(1, pf);
-    } else {
-      // fp32: block by block
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        qk_block(kb, s);
-        exp_block(kb, s, pf, ts);
-        if (!sums_ok(ts)) redo(kb, s, pf, ts);
-#pragma unroll
-        for (int qb = 0; qb < NQB; ++qb) l[qb] += ts[qb];
-        pv_block(kb, pf);
-      }
+      ts = expo(s);
     }
+    l += ts;
+#pragma unroll
+    for (int ch = 0; ch < NCH; ++ch)
+#pragma unroll
+      for (int db = 0; db < 2; ++db) o[db] = M::mma(read_v(cv, L::VP, db * 32 + l32, kb, ch, hi), s[ch], o[db]);
   };
 
   const int n = max(t1 - t0, 0);
-  if constexpr (DMA) {
-   if (n > 0) {
-    // Every iteration fetches and issues unconditionally: a split that has
-    // tiles reads at most three tiles past its end, which the gather list's
-    // padding covers (pad entries name the zero page).  So
-    // each iteration adds the same vector-memory operations, in the same
-    // order: the ids of tile i + 3 (NFETCH), then tile i + 2's data (NISSUE).
-    // Waiting until at most NISSUE are in flight at the end of iteration i
-    // leaves only tile i + 2's data outstanding: tile i + 1 has landed and
-    // the ids of tile i + 3 are in registers (the compiler counts the same
-    // way and adds no wait before they are used).
-    DL ld;
-    ld.init(h, a.H, tid);
-    typename DL::Ids ide, ido;  // ids of the tiles at even / odd distance from t0
-    i32x4 lc, l1, l2;           // entry lengths: this tile, next, next but one
-    const char* kp = (const char*)a.kpool;
-    const char* vp = (const char*)a.vpool;
-    char* lbase = (char*)&lt[0][0];
-    constexpr int BB = DL::BUF_BYTES;
-    auto ready = [](typename DL::Ids& x) {
-      asm volatile("" : "+v"(x.pg), "+v"(x.ln));
-    };
-    ld.fetch(a, t0, ide);
-    ld.fetch(a, t0 + 1, ido);
-    __builtin_amdgcn_s_waitcnt(0);  // the queries and the first ids
-#pragma unroll
-    for (int qb = 0; qb < NQB; ++qb)
-#pragma unroll
-      for (int dc = 0; dc < NDC; ++dc) asm volatile("" : "+v"(qf[qb][dc]));
-    ready(ide);
-    ready(ido);
-    asm volatile("" ::: "memory");
-    ld.issue(kp, vp, ide, lbase, wave);
-    lc = ide.ln;
-    ld.fetch(a, t0 + 2, ide);
-    ld.issue(kp, vp, ido, lbase + BB, wave);
-    l1 = ido.ln;
-    asm volatile("" ::: "memory");
-    wait_vmem<DL::NISSUE>();  // tile t0 and the ids of tile t0 + 2 have landed
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    auto step = [&](int i, typename DL::Ids& fx, const typename DL::Ids& iy) {
-      ld.fetch(a, t0 + i + 3, fx);
-      ld.issue(kp, vp, iy, lbase + ((i + 2) % 3) * BB, wave);
-      l2 = iy.ln;
-      asm volatile("" ::: "memory");  // the loads above stay ahead of the count below
-      const T* ck = lt[i % 3];
-      compute_tile(ck, ck + VOFF, lc);
-      asm volatile("" ::: "memory");
-      wait_vmem<DL::NISSUE>();
-      asm volatile("" ::: "memory");
-      __builtin_amdgcn_s_barrier();  // buffer i % 3 is free, tile i + 1 visible to all waves
-      asm volatile("" ::: "memory");
-      lc = l1;
-      l1 = l2;
-    };
-    for (int i = 0; i < n; i += 2) {
-      step(i, ido, ide);
-      if (i + 1 < n) step(i + 1, ide, ido);
+  L ld;
+  ld.init((const float*)a.kpool, (const float*)a.vpool, h, a.H, tid);
+  if (n > 0) {
+    ld.fetch_pages(a, t0, tid);
+    ld.fetch_data(tid);
+    ld.fetch_pages(a, t0 + 1, tid);
+    ld.store(lt[t0 & 1], tid);
+  }
+  i32x4 cur_lens = ld.dlen;  // entry lengths of the tile in LDS
+  __syncthreads();
+  for (int tile = t0; tile < t1; ++tile) {
+    const int buf = tile & 1;
+    const bool more = tile + 1 < t1;
+    if (more) {
+      ld.fetch_data(tid);                         // tile + 1, lands during this tile's math
+      ld.fetch_pages(a, tile + 2, tid);           // page ids two tiles ahead
     }
-    // the loads issued past the last tile land before the workgroup's LDS is released
-    wait_vmem<0>();
-   }
-  } else {
-    L ld;
-    ld.init(kpool, vpool, h, a.H, tid);
-    if (n > 0) {
-      ld.fetch_pages(a, t0, tid);
-      ld.fetch_data(tid);
-      ld.fetch_pages(a, t0 + 1, tid);
-      ld.store(lt[t0 & 1], tid);
-    }
-    i32x4 cur_lens = ld.dlen;  // entry lengths of the tile in LDS
+    block(lt[buf], lt[buf] + VOFF, cur_lens, 0);
+    block(lt[buf], lt[buf] + VOFF, cur_lens, 1);
+    // the other buffer was last read in the previous tile, before its barrier
+    if (more) ld.store(lt[buf ^ 1], tid);
+    cur_lens = ld.dlen;
     __syncthreads();
-    for (int tile = t0; tile < t1; ++tile) {
-      const int buf = tile & 1;
-      const bool more = tile + 1 < t1;
-      if (more) {
-        ld.fetch_data(tid);                         // tile + 1, lands during this tile's math
-        ld.fetch_pages(a, tile + 2, tid);           // page ids two tiles ahead
-      }
-      compute_tile(lt[buf], lt[buf] + VOFF, cur_lens);
-      // the other buffer was last read in the previous tile, before its barrier
-      if (more) ld.store(lt[buf ^ 1], tid);
-      cur_lens = ld.dlen;
-      __syncthreads();
-    }
   }
 
-  // Each lane summed P over its own half of the keys (rows 4*hi + ...); both
-  // halves share the running max, so the two partial sums simply add.
+  // each lane summed P over its own half of the keys; both halves share m
+  l += __shfl_xor(l, 32);
+  const int q = qbase + l32;
+  if (q >= a.Tq) return;
+  const bool empty = !(l > 0.f);
+  const float inv = empty ? 0.f : 1.f / l;
+  const float lse = empty ? -INFINITY : m * 0.69314718f + __logf(l);  // m is in log2 units
+  const size_t row = (size_t)q * a.H + h;
+  // O^T accumulators hold dims db*32 + 8*(r/4) + 4*hi + r%4
 #pragma unroll
-  for (int qb = 0; qb < NQB; ++qb) l[qb] += __shfl_xor(l[qb], 32);
-
-  // epilogue: O^T accumulators hold dims db*32 + 8*(r/4) + 4*hi + r%4
-  if constexpr (sizeof(T) == 2) {
-    if (a.S > 1) {
-      // split partials go out through LDS (free once every wave is past its
-      // last tile and no tile load is still landing): each wave stages its
-      // 64 queries x 32 dims of one half of the head dim as 128-byte rows
-      // (swizzled like the tiles), then every store instruction writes 8
-      // whole 128-byte lines instead of 32-byte pieces of 32 rows
-      static_assert(NBUF * BUF_ELEMS * sizeof(T) >= kWaves * QPW * 32 * 4, "staging fits the tile buffers");
-      wait_vmem<0>();
-      __syncthreads();
-      char* st = (char*)&lt[0][0] + wave * (QPW * 32 * 4);
-      float inv[NQB];
+  for (int db = 0; db < 2; ++db)
 #pragma unroll
-      for (int qb = 0; qb < NQB; ++qb) inv[qb] = l[qb] > 0.f ? 1.f / l[qb] : 0.f;
-#pragma unroll
-      for (int db = 0; db < 2; ++db) {
-#pragma unroll
-        for (int qb = 0; qb < NQB; ++qb)
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            floatx4 v;
-            v[0] = o[db][qb][g * 4 + 0] * inv[qb];
-            v[1] = o[db][qb][g * 4 + 1] * inv[qb];
-            v[2] = o[db][qb][g * 4 + 2] * inv[qb];
-            v[3] = o[db][qb][g * 4 + 3] * inv[qb];
-            *(floatx4*)(st + swz(qb * 32 + l32, 2 * g + hi)) = v;
-          }
-        __builtin_amdgcn_wave_barrier();
-        asm volatile("" ::: "memory");
-#pragma unroll
-        for (int it = 0; it < QPW / 8; ++it) {
-          const int row = it * 8 + (lane >> 3), c = lane & 7;
-          const floatx4 v = *(const floatx4*)(st + swz(row, c));
-          const int q = qbase + row;
-          if (q < a.Tq)
-            *(floatx4*)(a.o_part + (((size_t)split * a.Tq + q) * a.H + h) * kHeadDim + db * 32 + c * 4) = v;
-        }
-        __builtin_amdgcn_wave_barrier();
-        asm volatile("" ::: "memory");
+    for (int g = 0; g < 4; ++g) {
+      const int d = db * 32 + g * 8 + hi * 4;
+      floatx4 v;
+      v[0] = o[db][g * 4 + 0] * inv;
+      v[1] = o[db][g * 4 + 1] * inv;
+      v[2] = o[db][g * 4 + 2] * inv;
+      v[3] = o[db][g * 4 + 3] * inv;
+      if (a.S > 1) {
+        *(floatx4*)(a.o_part + ((size_t)split * a.Tq * a.H + row) * kHeadDim + d) = v;
+      } else if (a.out_bf16) {
+        bf16x4 w;
+        w[0] = (bf16)v[0]; w[1] = (bf16)v[1]; w[2] = (bf16)v[2]; w[3] = (bf16)v[3];
+        *(bf16x4*)((bf16*)a.out + row * kHeadDim + d) = w;
+      } else {
+        *(floatx4*)((float*)a.out + row * kHeadDim + d) = v;
       }
-#pragma unroll
-      for (int qb = 0; qb < NQB; ++qb) {
-        const int q = qbase + qb * 32 + l32;
-        if (q < a.Tq && hi == 0)
-          a.lse_part[((size_t)split * a.Tq + q) * a.H + h] =
-              l[qb] > 0.f ? m[qb] * 0.69314718f + __logf(l[qb]) : -INFINITY;
-      }
-      return;
     }
+  if (hi == 0) {
+    if (a.S > 1) a.lse_part[(size_t)split * a.Tq * a.H + row] = lse;
+    else if (a.lse) a.lse[row] = lse;
+  }
+}
+
+// Epilogue of the bf16 attention: O normalized by the row sum l (each lane
+// holds both halves' sums), written to the output with the LSE, or, with
+// S > 1, to this split's partial.  Partials go out through LDS (free once
+// every wave is past its last tile and no tile load is still landing): each
+// wave stages its 64 queries x 32 dims of one half of the head dim as
+// swizzled 128-byte rows, then every store instruction writes 8 whole
+// 128-byte lines instead of 32-byte pieces of 32 rows.
+__device__ inline void attn_epilogue_bf(const AttnArgs& a, const floatx16 (&o)[2][2], const float (&m)[2],
+                                        const float (&l)[2], int split, int qbase, int h, int l32, int hi,
+                                        int lane, int wave, char* lds) {
+  constexpr int NQB = 2, QPW = 64;
+  float inv[NQB];
+#pragma unroll
+  for (int qb = 0; qb < NQB; ++qb) inv[qb] = l[qb] > 0.f ? 1.f / l[qb] : 0.f;
+  if (a.S > 1) {
+    __syncthreads();
+    char* st = lds + wave * (QPW * 32 * 4);
+#pragma unroll
+    for (int db = 0; db < 2; ++db) {
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          floatx4 v;
+          v[0] = o[db][qb][g * 4 + 0] * inv[qb];
+          v[1] = o[db][qb][g * 4 + 1] * inv[qb];
+          v[2] = o[db][qb][g * 4 + 2] * inv[qb];
+          v[3] = o[db][qb][g * 4 + 3] * inv[qb];
+          *(floatx4*)(st + swz(qb * 32 + l32, 2 * g + hi)) = v;
+        }
+      __builtin_amdgcn_wave_barrier();
+      asm volatile("" ::: "memory");
+#pragma unroll
+      for (int it = 0; it < QPW / 8; ++it) {
+        const int row = it * 8 + (lane >> 3), c = lane & 7;
+        const floatx4 v = *(const floatx4*)(st + swz(row, c));
+        const int q = qbase + row;
+        if (q < a.Tq)
+          *(floatx4*)(a.o_part + (((size_t)split * a.Tq + q) * a.H + h) * kHeadDim + db * 32 + c * 4) = v;
+      }
+      __builtin_amdgcn_wave_barrier();
+      asm volatile("" ::: "memory");
+    }
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) {
+      const int q = qbase + qb * 32 + l32;
+      if (q < a.Tq && hi == 0)
+        a.lse_part[((size_t)split * a.Tq + q) * a.H + h] =
+            l[qb] > 0.f ? m[qb] * 0.69314718f + __logf(l[qb]) : -INFINITY;
+    }
+    return;
   }
 #pragma unroll
   for (int qb = 0; qb < NQB; ++qb) {
-    int q = qbase + qb * 32 + l32;
+    const int q = qbase + qb * 32 + l32;
     if (q >= a.Tq) continue;
-    bool empty = !(l[qb] > 0.f);
-    float inv = empty ? 0.f : 1.f / l[qb];
-    float lse = empty ? -INFINITY : m[qb] * 0.69314718f + __logf(l[qb]);  // m is in log2 units
-    size_t row = (size_t)q * a.H + h;
+    const float lse = l[qb] > 0.f ? m[qb] * 0.69314718f + __logf(l[qb]) : -INFINITY;  // m in log2 units
+    const size_t row = (size_t)q * a.H + h;
 #pragma unroll
     for (int db = 0; db < 2; ++db)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        int d = db * 32 + g * 8 + hi * 4;
+        const int d = db * 32 + g * 8 + hi * 4;
         floatx4 v;
-        v[0] = o[db][qb][g * 4 + 0] * inv;
-        v[1] = o[db][qb][g * 4 + 1] * inv;
-        v[2] = o[db][qb][g * 4 + 2] * inv;
-        v[3] = o[db][qb][g * 4 + 3] * inv;
-        if (a.S > 1) {
-          *(floatx4*)(a.o_part + ((size_t)split * a.Tq * a.H + row) * kHeadDim + d) = v;
-        } else if (a.out_bf16) {
+        v[0] = o[db][qb][g * 4 + 0] * inv[qb];
+        v[1] = o[db][qb][g * 4 + 1] * inv[qb];
+        v[2] = o[db][qb][g * 4 + 2] * inv[qb];
+        v[3] = o[db][qb][g * 4 + 3] * inv[qb];
+        if (a.out_bf16) {
           bf16x4 w;
           w[0] = (bf16)v[0]; w[1] = (bf16)v[1]; w[2] = (bf16)v[2]; w[3] = (bf16)v[3];
           *(bf16x4*)((bf16*)a.out + row * kHeadDim + d) = w;
@@ -1121,11 +979,300 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
           *(floatx4*)((float*)a.out + row * kHeadDim + d) = v;
         }
       }
-    if (hi == 0) {
-      if (a.S > 1) a.lse_part[(size_t)split * a.Tq * a.H + row] = lse;
-      else if (a.lse) a.lse[row] = lse;
-    }
+    if (hi == 0 && a.lse) a.lse[row] = lse;
   }
+}
+
+// ---------------------------------------------------------------------------
+// bf16 paged attention, software-pipelined over 32-key blocks.
+//
+// Workgroup shape, mapping and splits as in k_attn.  Step j of a wave issues,
+// independently of one another, the K.Q^T MFMAs of key block j + 1, the
+// softmax of block j (scaling, exponentials, packing, row sums: VALU) and the
+// P.V MFMAs of block j - 1, interleaved one MFMA to six VALU instructions, so
+// that one wave alone keeps both pipes of its SIMD busy.  Block j's sums are
+// checked at the end of step j, before its P.V in step j + 1.  A 64-key tile
+// (two blocks) is read for its K from the step before its first block's
+// softmax and for its V^T until the step after its last one: two tiles are in
+// use, one is landing and a fourth buffer is being filled.  Tiles go straight
+// from memory into four LDS buffers (global_load_lds), issued three tiles
+// ahead, with one barrier per tile.
+template <int P>
+__global__ __launch_bounds__(256, 2) void k_attn_bf(AttnArgs a) {
+  using M = Mfma<bf16>;
+  using Frag = bf16x8;
+  using DL = DmaLoader<P>;
+  constexpr int NQB = 2, NDC = 4, NCH = 2;
+  constexpr int BB = DL::BUF_BYTES;
+  __shared__ __attribute__((aligned(16))) char lt[4 * BB];
+
+  int h, split, qt, t0, t1;
+  if (!attn_place(a, h, split, qt, t0, t1)) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, hi = lane >> 5;
+  const int qbase = (qt * kWaves + wave) * 64;
+
+  Frag qf[NQB][NDC];
+  load_q(a, qbase, h, l32, hi, qf);
+  floatx16 o[2][NQB];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < NQB; ++j) o[i][j] = zero16();
+  // scores, lazy offsets and masks as in k_attn
+  const float qs = a.qk_scale;
+  constexpr float kNoKey = -1e20f;
+  constexpr float kMaxBlockSum = 65536.f;
+  constexpr float kRaise = 8.f;
+  float m[NQB], l[NQB], nm[NQB];
+#pragma unroll
+  for (int qb = 0; qb < NQB; ++qb) {
+    m[qb] = kNoKey;
+    nm[qb] = -kNoKey;
+    l[qb] = 0.f;
+  }
+
+  const int n = max(t1 - t0, 0);
+  if (n > 0) {
+    DL ld;
+    ld.init(h, a.H, tid);
+    const char* kp = (const char*)a.kpool;
+    const char* vp = (const char*)a.vpool;
+    auto buf = [&](int t) __attribute__((always_inline)) { return lt + (t & 3) * BB; };
+    // mask bits of a tile: bit kb set when key kb*32 + l32 is masked
+    auto minfo = [&](const typename DL::Ids& x) __attribute__((always_inline)) {
+      int r = 0;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) r |= key_masked<P>(x.ln, kb * 32 + l32) ? 1 << kb : 0;
+      return r;
+    };
+    auto ready = [](typename DL::Ids& x) __attribute__((always_inline)) { asm volatile("" : "+v"(x.pg), "+v"(x.ln)); };
+
+    // raw scores of key block kb of the tile in buffer b (mask bits mi)
+    auto qk_raw = [&](const char* b, int kb, int mi, floatx16 (&s)[NQB]) __attribute__((always_inline)) {
+      Frag kf[NDC];
+#pragma unroll
+      for (int dc = 0; dc < NDC; ++dc) kf[dc] = read_k((const bf16*)b, 0, kb * 32 + l32, dc, hi);
+      const floatx16 s0 = M::mma_seed(M::mask_a((mi >> kb) & 1, hi), M::mask_b(hi));
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) {
+        s[qb] = M::mma(kf[0], qf[qb][0], s0);
+#pragma unroll
+        for (int dc = 1; dc < NDC; ++dc) s[qb] = M::mma(kf[dc], qf[qb][dc], s[qb]);
+      }
+    };
+    auto softmax = [&](floatx16 (&s)[NQB], Frag (&p)[NCH][NQB], float (&ts)[NQB]) __attribute__((always_inline)) {
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) {
+        ts[qb] = 0.f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[qb][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][r], qs, nm[qb]));
+#pragma unroll
+        for (int ch = 0; ch < NCH; ++ch) {
+          p[ch][qb] = pack_p(s[qb], ch, bf16());
+          ts[qb] = rowsum_add(ts[qb], p[ch][qb]);
+        }
+      }
+    };
+    // One step: K.Q^T of block qkb of buffer qbuf into sQ (mask bits qmi),
+    // softmax of sS into pS, P.V of pV with block vkb of buffer vbuf.  Issued
+    // in 17 groups, each an MFMA and six VALU instructions of the softmax (two
+    // elements: their scaled logits and exponentials, one bf16 pack, one
+    // row-sum dot product), kept in this order by scheduling barriers: the
+    // mask product first (no LDS operand), the K.Q^T MFMAs while the V^T
+    // fragments land, then the P.V MFMAs.
+    auto step = [&](const char* qbuf, int qkb, int qmi, const char* vbuf, int vkb, floatx16 (&sQ)[NQB],
+                    floatx16 (&sS)[NQB], Frag (&pS)[NCH][NQB], const Frag (&pV)[NCH][NQB], float (&ts)[NQB])
+        __attribute__((always_inline)) {
+      typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+      bf16x2 one;
+      one[0] = (bf16)1.0f;
+      one[1] = (bf16)1.0f;
+      // K fragments dc = 0, 1 now, 2 and 3 two groups before their MFMAs;
+      // the V^T fragments likewise, spread over groups 3 .. 7
+      Frag kf[NDC];
+#pragma unroll
+      for (int dc = 0; dc < 2; ++dc) kf[dc] = read_k((const bf16*)qbuf, 0, qkb * 32 + l32, dc, hi);
+      ts[0] = 0.f;
+      ts[1] = 0.f;
+      // softmax work of group g: the scaled logits and exponentials of
+      // elements 2i, 2i + 1 of query block qb = g / 8 (pair g), and the bf16
+      // pack and row-sum dot product of pair g - 1, whose exponentials were
+      // issued a group earlier (pair 16 closes the step)
+      float xe[2];
+      auto valu = [&](int g) __attribute__((always_inline)) {
+        float xn[2];
+        if (g < 16) {
+          const int qb = g >> 3, i = g & 7;
+          xn[0] = __builtin_fmaf(sS[qb][2 * i], qs, nm[qb]);
+          xn[1] = __builtin_fmaf(sS[qb][2 * i + 1], qs, nm[qb]);
+        }
+        if (g > 0) {
+          const int gp = g - 1, qb = gp >> 3, i = gp & 7, ch = i >> 2, k = i & 3;
+          bf16x2 pr;
+          pr[0] = (bf16)xe[0];
+          pr[1] = (bf16)xe[1];
+          pS[ch][qb][2 * k] = pr[0];
+          pS[ch][qb][2 * k + 1] = pr[1];
+          ts[qb] = __builtin_amdgcn_fdot2_f32_bf16(pr, one, ts[qb], false);
+        }
+        if (g < 16) {
+          xe[0] = __builtin_amdgcn_exp2f(xn[0]);
+          xe[1] = __builtin_amdgcn_exp2f(xn[1]);
+        }
+      };
+      // group 0: the mask product (all zero in a full tile)
+      const floatx16 s0 = M::mma_seed(M::mask_a((qmi >> qkb) & 1, hi), M::mask_b(hi));
+      valu(0);
+      __builtin_amdgcn_sched_barrier(0);
+      Frag vf[NCH][2];
+      // groups 1 .. 8: K.Q^T (the V^T fragments read after the first two)
+#pragma unroll
+      for (int g = 0; g < 8; ++g) {
+        const int dc = g >> 1, qb = g & 1;
+        sQ[qb] = M::mma(kf[dc], qf[qb][dc], dc == 0 ? s0 : sQ[qb]);
+        if (g < 7) valu(g + 1);
+        if (g == 0 || g == 2) kf[2 + g / 2] = read_k((const bf16*)qbuf, 0, qkb * 32 + l32, 2 + g / 2, hi);
+        if (g >= 3 && g < 7) {
+          const int c = (g - 3) >> 1, db = (g - 3) & 1;
+          vf[c][db] = read_v((const bf16*)(vbuf + DL::KBYTES), 0, db * 32 + l32, vkb, c, hi);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // groups 9 .. 16: P.V
+#pragma unroll
+      for (int g = 0; g < 8; ++g) {
+        const int c = g >> 2, db = (g >> 1) & 1, qb = g & 1;
+        o[db][qb] = M::mma(vf[c][db], pV[c][qb], o[db][qb]);
+        valu(g + 8);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      valu(16);
+    };
+    // the sum check of block kb of buffer b after its softmax: if some lane's
+    // sum exceeds 2^16, the block's raw scores again (its tile is still in
+    // LDS), m raised to the block max where that exceeds it by more than
+    // kRaise (O and l rescaled), then the softmax again
+    auto settle = [&](const char* b, int kb, int mi, floatx16 (&s)[NQB], Frag (&p)[NCH][NQB], float (&ts)[NQB])
+        __attribute__((always_inline)) {
+      bool bad = false;
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) bad = bad || !(ts[qb] <= kMaxBlockSum);
+      if (__any(bad)) {
+        qk_raw(b, kb, mi, s);
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb) {
+          float x = s[qb][0];
+#pragma unroll
+          for (int r = 1; r < 16; ++r) x = fmaxf(x, s[qb][r]);
+          const float mx = half_swap_max(x) * qs;  // masked keys sit near -1e30 * qs < kNoKey
+          if (mx > m[qb] + kRaise) {
+            const float alpha = __builtin_amdgcn_exp2f(m[qb] - mx);
+            m[qb] = mx;
+            nm[qb] = -mx;
+            o[0][qb] *= alpha;
+            o[1][qb] *= alpha;
+            l[qb] *= alpha;
+          }
+        }
+        softmax(s, p, ts);
+      }
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) l[qb] += ts[qb];
+    };
+
+    // Prologue: page ids and lengths of tiles t0 .. t0 + 3, then the data of
+    // t0 .. t0 + 2.  From then on every tile period issues the ids of tile
+    // t + 4 and then tile t + 3's data (four loads) after its barrier, so
+    // waiting for all but the last four vector-memory operations before the
+    // next barrier leaves only the newest tile's data in flight: the tile
+    // needed next has landed and the ids to issue have arrived.
+    typename DL::Ids ida, idb, idc, idd;
+    ld.fetch(a, t0, ida);
+    ld.fetch(a, t0 + 1, idb);
+    ld.fetch(a, t0 + 2, idc);
+    ld.fetch(a, t0 + 3, idd);
+    __builtin_amdgcn_s_waitcnt(0);  // the queries and the ids
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb)
+#pragma unroll
+      for (int dc = 0; dc < NDC; ++dc) asm volatile("" : "+v"(qf[qb][dc]));
+    ready(ida);
+    ready(idb);
+    ready(idc);
+    ready(idd);
+    asm volatile("" ::: "memory");
+    ld.issue(kp, vp, ida, buf(t0), wave);
+    ld.issue(kp, vp, idb, buf(t0 + 1), wave);
+    ld.issue(kp, vp, idc, buf(t0 + 2), wave);
+    // mask bits of tiles t, t + 1, t + 2 in bits 0-1, 2-3, 4-5
+    int mr = minfo(ida) | minfo(idb) << 2 | minfo(idc) << 4;
+    idb = idd;  // the ids of tile t0 + 3, used in the first period
+    asm volatile("" ::: "memory");
+    wait_vmem<2 * DL::NISSUE>();  // tile t0 has landed
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+
+    floatx16 s0[NQB], s1[NQB];
+    Frag p0[NCH][NQB], p1[NCH][NQB];
+#pragma unroll
+    for (int ch = 0; ch < NCH; ++ch)
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) p1[ch][qb] = Frag{};  // the P.V of step 0 adds nothing
+    float ts[NQB];
+    qk_raw(buf(t0), 0, mr & 3, s0);
+
+    // one tile period; `use` holds the ids of tile t + 3, `next` receives those of t + 4
+    auto period = [&](int i, typename DL::Ids& use, typename DL::Ids& next) __attribute__((always_inline)) {
+      const int t = t0 + i;
+      // step 2i: QK of block 1 of tile t, softmax of block 0 of tile t, P.V of
+      // block 1 of tile t - 1 (of tile t with P = 0 in the first step)
+      step(buf(t), 1, mr & 3, buf(i > 0 ? t - 1 : t), 1, s1, s0, p0, p1, ts);
+      settle(buf(t), 0, mr & 3, s0, p0, ts);
+      // tile t + 1 has landed; tile t - 1's buffer is free: ids of tile t + 4,
+      // data of tile t + 3 (past the split's end they are read and unused)
+      asm volatile("" ::: "memory");
+      wait_vmem<DL::NISSUE>();
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      ready(use);
+      ld.fetch(a, t + 4, next);
+      ld.issue(kp, vp, use, buf(t + 3), wave);
+      mr |= minfo(use) << 6;
+      asm volatile("" ::: "memory");
+      // step 2i + 1: QK of block 0 of tile t + 1, softmax of block 1 of tile t,
+      // P.V of block 0 of tile t
+      step(buf(t + 1), 0, (mr >> 2) & 3, buf(t), 0, s0, s1, p1, p0, ts);
+      settle(buf(t), 1, mr & 3, s1, p1, ts);
+      mr >>= 2;
+    };
+    // after the prologue idb holds the ids of tile t0 + 3
+    for (int i = 0; i < n; i += 2) {
+      period(i, idb, ida);
+      if (i + 1 < n) period(i + 1, ida, idb);
+    }
+    // the last block's P.V
+    {
+      const char* vb = buf(t0 + n - 1);
+#pragma unroll
+      for (int ch = 0; ch < NCH; ++ch)
+#pragma unroll
+        for (int db = 0; db < 2; ++db) {
+          const Frag vf = read_v((const bf16*)(vb + DL::KBYTES), 0, db * 32 + l32, 1, ch, hi);
+#pragma unroll
+          for (int qb = 0; qb < NQB; ++qb) o[db][qb] = M::mma(vf, p1[ch][qb], o[db][qb]);
+        }
+    }
+    // the loads issued past the last tile land before the workgroup's LDS is reused
+    wait_vmem<0>();
+  }
+
+  // each lane summed P over its own half of the keys
+#pragma unroll
+  for (int qb = 0; qb < NQB; ++qb) l[qb] += __shfl_xor(l[qb], 32);
+  attn_epilogue_bf(a, o, m, l, split, qbase, h, l32, hi, lane, wave, lt);
 }
 
 // Split merge: 16 threads per (token, head) row, 4 dims each; all partial
@@ -1241,12 +1388,12 @@ hipError_t launch_attn(int dtype, const AttnArgs& a, hipStream_t s) {
   int groups = (a.n_units + kNumXcd - 1) / kNumXcd;
   dim3 grid(groups * kNumXcd * a.n_qtiles);
   switch (dtype * 100 + a.P) {
-    case 116: hipLaunchKernelGGL((k_attn<bf16, 16>), grid, dim3(256), 0, s, a); break;
-    case 132: hipLaunchKernelGGL((k_attn<bf16, 32>), grid, dim3(256), 0, s, a); break;
-    case 164: hipLaunchKernelGGL((k_attn<bf16, 64>), grid, dim3(256), 0, s, a); break;
-    case 16: hipLaunchKernelGGL((k_attn<float, 16>), grid, dim3(256), 0, s, a); break;
-    case 32: hipLaunchKernelGGL((k_attn<float, 32>), grid, dim3(256), 0, s, a); break;
-    case 64: hipLaunchKernelGGL((k_attn<float, 64>), grid, dim3(256), 0, s, a); break;
+    case 116: hipLaunchKernelGGL((k_attn_bf<16>), grid, dim3(256), 0, s, a); break;
+    case 132: hipLaunchKernelGGL((k_attn_bf<32>), grid, dim3(256), 0, s, a); break;
+    case 164: hipLaunchKernelGGL((k_attn_bf<64>), grid, dim3(256), 0, s, a); break;
+    case 16: hipLaunchKernelGGL((k_attn<16>), grid, dim3(256), 0, s, a); break;
+    case 32: hipLaunchKernelGGL((k_attn<32>), grid, dim3(256), 0, s, a); break;
+    case 64: hipLaunchKernelGGL((k_attn<64>), grid, dim3(256), 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
