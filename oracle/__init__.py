@@ -29,6 +29,8 @@ class _Cfg(C.Structure):
         ("max_frames", C.c_int64),
         ("num_pages", C.c_int32),
         ("ring_init", C.POINTER(C.c_int32)),
+        ("window", C.c_int32),
+        ("overlap", C.c_int32),
     ]
 
 
@@ -70,6 +72,8 @@ def lib():
         L.orc_default_compact.argtypes = [C.c_int32, C.c_int32, C.c_int32, i32p]
         L.orc_default_num_pages.restype = C.c_int64
         L.orc_default_num_pages.argtypes = [C.POINTER(_Cfg)]
+        L.orc_rope_position.restype = C.c_int64
+        L.orc_rope_position.argtypes = [C.c_void_p, C.c_int64]
         _lib = L
     return _lib
 
@@ -98,6 +102,8 @@ class OracleConfig:
     max_frames: int = 64
     num_pages: int = 0
     ring_init: list | None = None
+    window: int = 0      # windowed inference: frames per window (0 = off)
+    overlap: int = 0     # keyframes carried into the next window
     _keep: list = field(default_factory=list, repr=False)
 
     def to_c(self) -> _Cfg:
@@ -120,6 +126,7 @@ class OracleConfig:
             arr = np.asarray(self.ring_init, dtype=np.int32)
             self._keep.append(arr)
             c.ring_init = _p(arr, C.c_int32)
+        c.window, c.overlap = self.window, self.overlap
         return c
 
 
@@ -188,6 +195,10 @@ class OracleCache:
 
     def n_ctx(self) -> int:
         return int(lib().orc_n_ctx(self.h))
+
+    def rope_position(self, frame: int) -> int:
+        """temporal rotary position of `frame` (window-relative in windowed mode)"""
+        return int(lib().orc_rope_position(self.h, frame))
 
     def select(self):
         cap = self.N + 8

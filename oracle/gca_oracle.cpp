@@ -27,6 +27,16 @@
 //    streaming starts (section "Streaming Inference API" and the same FAQ).
 //    Read as: append those frames, then every one of their queries, rotated
 //    at its own frame index, attends over the context that then exists.
+//  * Windowed inference ("LingBot-Map runs 10,000 frames on monocular video",
+//    section "Cloning and Installing"; the project summary's "Main features"
+//    table): past the range the video rotary embedding was trained on, the
+//    memory slides as fixed-size windows that overlap by a few keyframes.
+//    Read as: a window spans `window` frames from its origin, and a frame's
+//    temporal rotary position is its index relative to that origin.  The
+//    first frame outside the window starts the next one: the cache is reset,
+//    the last `overlap` keyframes that fit in a window with the new frame are
+//    appended again from their raw K/V (oldest first, at positions relative
+//    to the new origin, which is the oldest of them), then the frame itself.
 //
 // Readings where the pages are silent (each is a choice, mirrored by the HIP
 // library's own independent code):
@@ -74,6 +84,7 @@ struct Cfg {
   long long max_frames;
   int num_pages;
   std::vector<int> ring_init;
+  int window, overlap;  // windowed inference: frames per window (0 = off), overlap keyframes
 };
 
 // ---- rounding to the storage type -----------------------------------------
@@ -172,6 +183,12 @@ struct Frame {
   std::vector<int> pages;   // allocator model: ceil(T/P) page ids
 };
 
+// a keyframe's raw (un-rotated) K/V, kept for the next window's overlap
+struct RawFrame {
+  long long idx;
+  std::vector<float> k, v;  // empty for a frame appended without data
+};
+
 struct Cache {
   Cfg c;
   int ppf;
@@ -191,6 +208,9 @@ struct Cache {
   std::vector<int> ring;  // size N
   long long head = 0, tail = 0;  // monotonic counters, slot = counter mod N
   std::vector<int> traj_pages;
+  // windowed inference
+  long long origin = 0;          // frame index of the window's temporal position 0
+  std::deque<RawFrame> overlap;  // raw K/V of the window's last keyframes (at most `overlap`)
 };
 
 int pop_page(Cache& s) {
@@ -221,6 +241,8 @@ void reset(Cache& s) {
   s.head = 0;
   s.tail = s.N;
   s.traj_pages.clear();
+  s.origin = 0;
+  s.overlap.clear();
 }
 
 int page_len_frame(const Cache& s, int i) {
@@ -245,6 +267,8 @@ struct orc_config {
   int64_t max_frames;
   int32_t num_pages;           // 0 -> peak occupancy of a keyframe stream
   const int32_t* ring_init;    // NULL -> identity order
+  int32_t window;              // windowed inference: frames per window (0 = off)
+  int32_t overlap;             // keyframes carried into the next window
 };
 
 // Default compact offsets: special tokens first, then C - S evenly spaced patches.
@@ -256,10 +280,12 @@ void orc_default_compact(int32_t T, int32_t num_special, int32_t C, int32_t* out
 }
 
 // Pages needed at the peak of a keyframe stream: anchors, W+1 window frames
-// (append precedes evict), and the trajectory pages of every possible eviction.
+// (append precedes evict), and the trajectory pages of every possible eviction
+// (in windowed mode at most a window's frames are cached between resets).
 int64_t orc_default_num_pages(const orc_config* c) {
   long long ppf = (c->T + c->P - 1) / c->P;
-  long long evictions = std::max<long long>(0, c->max_frames - c->A - c->W);
+  long long span = c->window > 0 ? std::min<long long>(c->max_frames, c->window) : c->max_frames;
+  long long evictions = std::max<long long>(0, span - c->A - c->W);
   long long traj_tokens = (long long)c->C * evictions;
   long long traj_pages = (traj_tokens + c->P - 1) / c->P;
   return (long long)c->A * ppf + (long long)(c->W + 1) * ppf + traj_pages;
@@ -267,7 +293,8 @@ int64_t orc_default_num_pages(const orc_config* c) {
 
 void* orc_create(const orc_config* in) {
   if (!in || in->T <= 0 || in->H <= 0 || in->D <= 0 || in->D % 2 || in->P <= 0 || in->W < 1 ||
-      in->A < 0 || in->C < 0 || in->C > in->T || in->max_frames <= 0)
+      in->A < 0 || in->C < 0 || in->C > in->T || in->max_frames <= 0 || in->window < 0 || in->overlap < 0 ||
+      (in->window > 0 && (in->overlap < 1 || in->overlap > in->A + in->W || in->overlap >= in->window)))
     return nullptr;
   Cache* s = new Cache();
   Cfg& c = s->c;
@@ -279,6 +306,8 @@ void* orc_create(const orc_config* in) {
   c.num_special = in->num_special; c.grid_h = in->grid_h; c.grid_w = in->grid_w;
   c.rope = in->rope; c.theta = in->rope_theta; c.scale = in->sm_scale;
   c.max_frames = in->max_frames;
+  c.window = in->window;
+  c.overlap = in->window > 0 ? in->overlap : 0;
   c.num_pages = in->num_pages > 0 ? in->num_pages : (int)orc_default_num_pages(in);
   if (in->ring_init) c.ring_init.assign(in->ring_init, in->ring_init + c.num_pages);
   s->ppf = (c.T + c.P - 1) / c.P;
@@ -292,22 +321,17 @@ void orc_reset(void* h) { reset(*(Cache*)h); }
 int32_t orc_num_pages(void* h) { return ((Cache*)h)->N; }
 int32_t orc_pages_per_frame(void* h) { return ((Cache*)h)->ppf; }
 
-// Append one frame (raw, un-rotated K and V of shape [T][H][D]).  temp != 0
-// marks a non-keyframe that will be rolled back after attention.
-int orc_append(void* h, int64_t frame, const float* k, const float* v, int32_t temp) {
-  Cache& s = *(Cache*)h;
-  if (s.temp_pending) return E_SEQ;
-  if (s.has_last && frame <= s.last_frame) return E_SEQ;
-  if (frame < 0 || frame >= s.c.max_frames) return E_CAP;
+// Append one frame at temporal rotary position t (the global frame index, or
+// in windowed mode the index relative to the window's origin).
+static int append_at(Cache& s, int64_t frame, long long t, const float* k, const float* v, int32_t temp) {
   if (free_pages(s) < s.ppf) return E_PAGES;
   Frame f;
   f.idx = frame;
   // k == v == NULL appends a frame for bookkeeping only (page tables, gather
   // lists); such a cache cannot attend or materialise its context.
-  if ((k == nullptr) != (v == nullptr)) return E_ARG;
   if (k) {
-    f.k = prepare(s.c, frame, k, true);
-    f.v = prepare(s.c, frame, v, false);
+    f.k = prepare(s.c, t, k, true);
+    f.v = prepare(s.c, t, v, false);
   } else {
     s.data_less = true;
   }
@@ -323,6 +347,56 @@ int orc_append(void* h, int64_t frame, const float* k, const float* v, int32_t t
     s.window.push_back(std::move(f));
   }
   return OK;
+}
+
+// Append one frame (raw, un-rotated K and V of shape [T][H][D]).  temp != 0
+// marks a non-keyframe that will be rolled back after attention.  In windowed
+// mode the first frame outside the window starts the next window first.
+int orc_append(void* h, int64_t frame, const float* k, const float* v, int32_t temp) {
+  Cache& s = *(Cache*)h;
+  if (s.temp_pending) return E_SEQ;
+  if (s.has_last && frame <= s.last_frame) return E_SEQ;
+  if (frame < 0 || frame >= s.c.max_frames) return E_CAP;
+  if ((k == nullptr) != (v == nullptr)) return E_ARG;
+  if (s.c.window > 0 && !s.has_last) s.origin = frame;  // the first frame opens the first window
+  if (s.c.window > 0 && s.has_last && frame - s.origin >= s.c.window) {
+    // the next window: the last keyframes that fit in one window with this
+    // frame, oldest first; the oldest of them (or the frame) is the origin
+    std::vector<RawFrame> keep;
+    for (auto& r : s.overlap)
+      if (frame - r.idx < s.c.window) keep.push_back(std::move(r));
+    const bool dl = s.data_less;
+    reset(s);
+    s.data_less = dl;
+    s.origin = keep.empty() ? frame : keep.front().idx;
+    for (auto& r : keep) {
+      int rc = append_at(s, r.idx, r.idx - s.origin, r.k.empty() ? nullptr : r.k.data(),
+                         r.v.empty() ? nullptr : r.v.data(), 0);
+      if (rc) return rc;
+      s.overlap.push_back(std::move(r));
+    }
+  }
+  int rc = append_at(s, frame, s.c.window > 0 ? frame - s.origin : frame, k, v, temp);
+  if (rc) return rc;
+  if (s.c.window > 0 && !temp) {
+    RawFrame r;
+    r.idx = frame;
+    if (k) {
+      size_t n = (size_t)s.c.T * s.c.H * s.c.D;
+      r.k.assign(k, k + n);
+      r.v.assign(v, v + n);
+    }
+    s.overlap.push_back(std::move(r));
+    while ((int)s.overlap.size() > s.c.overlap) s.overlap.pop_front();
+  }
+  return OK;
+}
+
+// Temporal rotary position of a frame: its global index, or in windowed mode
+// its index relative to the window's origin.
+int64_t orc_rope_position(void* h, int64_t frame) {
+  Cache& s = *(Cache*)h;
+  return s.c.window > 0 ? frame - s.origin : frame;
 }
 
 // Evict window frames beyond W: keep their compact tokens in the trajectory and
@@ -582,8 +656,8 @@ int orc_attend(void* h, int64_t frame, const float* q, const int32_t* rows, int3
   // 1. materialise the selected context contiguously
   std::vector<float> K((size_t)n * hd), V((size_t)n * hd);
   orc_context(h, K.data(), V.data(), nullptr, nullptr, n);
-  // 2. rotate and round the queries
-  std::vector<float> Qp = prepare(c, frame, q, true);
+  // 2. rotate and round the queries (window-relative position in windowed mode)
+  std::vector<float> Qp = prepare(c, orc_rope_position(h, frame), q, true);
   // 3. softmax attention per (row, head), float64
   attend_over(c, K, V, n, Qp, rows, n_rows, out, lse, threads);
   return OK;
@@ -605,7 +679,7 @@ int orc_attend_frames(void* h, int64_t first, int32_t nf, const float* q, const 
   std::vector<float> K((size_t)n * hd), V((size_t)n * hd);
   orc_context(h, K.data(), V.data(), nullptr, nullptr, n);
   for (int i = 0; i < nf; ++i) {
-    std::vector<float> Qp = prepare(c, first + i, q + (size_t)i * c.T * hd, true);
+    std::vector<float> Qp = prepare(c, orc_rope_position(h, first + i), q + (size_t)i * c.T * hd, true);
     attend_over(c, K, V, n, Qp, rows, n_rows, out + (size_t)i * n_rows * hd,
                 lse ? lse + (size_t)i * n_rows * c.H : nullptr, threads);
   }

@@ -22,6 +22,7 @@ struct orc_config {
   int64_t max_frames;
   int32_t num_pages;
   const int32_t* ring_init;
+  int32_t window, overlap;
 };
 void* orc_create(const orc_config*);
 void orc_destroy(void*);
@@ -40,6 +41,7 @@ void orc_rope(const orc_config*, int64_t, const float*, double*);
 int orc_attend(void*, int64_t, const float*, const int32_t*, int32_t, double*, double*, int32_t);
 int orc_attend_frames(void*, int64_t, int32_t, const float*, const int32_t*, int32_t, double*, double*,
                       int32_t);
+int64_t orc_rope_position(void*, int64_t);
 void orc_default_compact(int32_t, int32_t, int32_t, int32_t*);
 }
 
@@ -111,6 +113,7 @@ int main() {
   c.A = 1; c.W = 2; c.C = 1; c.compact_idx = nullptr;
   c.num_special = 0; c.grid_h = 8; c.grid_w = 8; c.rope = 0;
   c.rope_theta = 10000.0; c.sm_scale = 0.125; c.num_pages = 0; c.ring_init = nullptr;
+  c.window = 0; c.overlap = 0;
   run(c, 8, 1, 0, 1);
   c.bf16 = 1; c.rope = 1; c.T = 36; c.num_special = 3; c.grid_h = 3; c.grid_w = 11; c.C = 5; c.P = 32;
   run(c, 12, 3, 0, 2);
@@ -118,6 +121,11 @@ int main() {
   run(c, 7, 2, 3, 3);
   c.A = 0; c.W = 3; c.C = 0;
   run(c, 10, 1, 0, 4);
+  // windowed inference: windows of 5 frames overlapping by 2 keyframes
+  c.A = 1; c.W = 2; c.C = 3; c.window = 5; c.overlap = 2;
+  run(c, 17, 1, 0, 5);
+  run(c, 17, 2, 0, 6);
+  c.window = 0; c.overlap = 0;
   std::vector<double> y((size_t)c.T * c.H * c.D);
   std::vector<float> x(y.size(), 1.f);
   orc_rope(&c, 5, x.data(), y.data());

@@ -663,3 +663,115 @@ def test_scale_frames_sequence_errors():
     for first, qq in [(1, q), (0, q[:2]), (-1, q[:1])]:
         with pytest.raises(RuntimeError):
             c.attend_frames(first, qq)
+
+
+# --------------------------------------------------------------------------- windowed inference
+#
+# Reading of windowed inference ("LingBot-Map runs 10,000 frames on monocular
+# video", section "Cloning and Installing"; the project summary's "Main
+# features" table): a window spans `window` frames from its origin and a
+# frame's temporal rotary position is its index relative to that origin; the
+# first frame outside the window starts the next one: the cache is reset, the
+# last `overlap` keyframes that fit in a window with that frame are appended
+# again (oldest first, the oldest becoming the origin), then the frame.
+
+
+def _wcfg(**kw):
+    d = dict(T=64, H=2, D=64, P=16, dtype="f32", A=1, W=2, C=1, max_frames=64, window=6, overlap=2)
+    d.update(kw)
+    return oracle.OracleConfig(**d)
+
+
+@pytest.mark.parametrize("interval,expected", [
+    # worked by hand: T = 64 tokens, anchor 1, window 2 keyframes, 1 compact token,
+    # windows of 6 frames overlapping by 2 keyframes
+    (1, dict(n_ctx=[64, 128, 192, 193, 194, 195, 192, 193, 194, 195, 192, 193, 194, 195],
+             pos=[0, 1, 2, 3, 4, 5, 2, 3, 4, 5, 2, 3, 4, 5],
+             live={6: [4, 5, 6], 13: [8, 12, 13]}, traj={13: [9, 10, 11]})),
+    # keyframes 0, 2, 4, ...; a non-keyframe is seen with the cache, then rolled back
+    (2, dict(n_ctx=[64, 128, 128, 192, 192, 256, 192, 256, 192, 256, 192, 256],
+             pos=[0, 1, 2, 3, 4, 5, 4, 5, 4, 5, 4, 5],
+             live={6: [2, 4, 6], 8: [4, 6, 8], 11: [6, 8, 10, 11]}, traj={})),   # 11: pending
+])
+def test_windowed_stream_hand_derived(interval, expected):
+    c = oracle.OracleCache(_wcfg())
+    fs = FrameStream(7, 64, 2, 64, "f32")
+    for f in range(len(expected["n_ctx"])):
+        key = f % interval == 0
+        k, v = fs.kv(f)
+        assert c.append(f, k, v, temp=not key) == 0
+        if key:
+            assert c.evict() == 0
+        assert c.n_ctx() == expected["n_ctx"][f], f
+        assert c.rope_position(f) == expected["pos"][f], f
+        if f in expected["live"]:
+            st = c.state()
+            assert st["frame_idx"].tolist() == expected["live"][f], f
+        if f in expected["traj"]:
+            tags = c.context()[2]
+            assert sorted(set(tags[c.n_ctx() - len(expected["traj"][f]):].tolist())) == expected["traj"][f]
+        if not key:
+            assert c.rollback(f) == 0
+
+
+@pytest.mark.parametrize("interval", [1, 2])
+def test_windowed_restart_is_a_fresh_cache_of_the_overlap_frames(interval):
+    """Right after a window starts, the cache holds what a fresh (non-windowed)
+    cache holds when fed the overlap keyframes and the new frame at their
+    window-relative indices: the same context rows bit for bit and the same
+    attention outputs; also against the rotary embedding evaluated directly at
+    the window-relative position."""
+    T, H = 36, 2
+    kw = dict(T=T, H=H, dtype="bf16", rope=1, num_special=3, grid_h=3, grid_w=11, A=1, W=3, C=4,
+              window=9, overlap=3, max_frames=40)
+    cw = oracle.OracleCache(_wcfg(**kw))
+    fs = FrameStream(11, T, H, 64, "bf16")
+    starts = []
+    for f in range(30):
+        key = f % interval == 0
+        k, v = fs.kv(f)
+        before = cw.rope_position(f - 1) if f else 0
+        assert cw.append(f, k, v, temp=not key) == 0
+        if key:
+            assert cw.evict() == 0
+        origin = f - cw.rope_position(f)
+        if f and origin != (f - 1) - before:
+            starts.append((f, origin))
+            keys = [g for g in range(origin, f) if g % interval == 0]
+            assert 1 <= len(keys) <= 3
+            fresh = oracle.OracleCache(oracle.OracleConfig(**{**kw, "window": 0, "overlap": 0}))
+            for g in keys:
+                kg, vg = fs.kv(g)
+                assert fresh.append(g - origin, kg, vg) == 0 and fresh.evict() == 0
+            assert fresh.append(f - origin, k, v, temp=not key) == 0
+            if key:
+                assert fresh.evict() == 0
+            a, b = cw.context(), fresh.context()
+            np.testing.assert_array_equal(a[0], b[0])
+            np.testing.assert_array_equal(a[1], b[1])
+            assert (a[2] - origin).tolist() == b[2].tolist()
+            q = fs.q(f)
+            oa, la = cw.attend(f, q)
+            ob, lb = fresh.attend(f - origin, q)
+            np.testing.assert_array_equal(oa, ob)
+            np.testing.assert_array_equal(la, lb)
+            # the new frame's keys: rotated at the window-relative position
+            cfg1 = oracle.OracleConfig(**{**kw, "window": 0, "overlap": 0})
+            ref = oracle.rope(cfg1, f - origin, k)
+            m, e = np.frexp(ref)
+            newest = a[0][np.where(a[2] == f)[0]]
+            np.testing.assert_array_equal(newest.astype(np.float64), np.ldexp(np.rint(m * 256.0), e - 8))
+        assert 0 <= cw.rope_position(f) < 9
+        if not key:
+            assert cw.rollback(f) == 0
+    assert len(starts) >= 3
+
+
+def test_windowed_config_rules():
+    assert oracle.default_num_pages(_wcfg(max_frames=1000)) == 4 + 12 + 1   # C*(6-1-2)=3 tokens: 1 page
+    with pytest.raises(ValueError):
+        oracle.OracleCache(_wcfg(overlap=0))
+    with pytest.raises(ValueError):
+        oracle.OracleCache(_wcfg(overlap=4))        # more than anchor + window keyframes
+    with pytest.raises(ValueError):
+        oracle.OracleCache(_wcfg(window=2, overlap=2))
