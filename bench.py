@@ -437,7 +437,8 @@ def run_cpu_baseline(w, n_ctx):
     fs = FrameStream(w.seed, w.T, w.H, w.D, w.dtype, n_base=w.n_base, drift_sigma=w.drift_sigma)
     cfg = oracle.OracleConfig(T=w.T, H=w.H, D=w.D, P=w.P, dtype=w.dtype, A=w.A, W=w.W, C=w.C,
                               rope=w.rope, num_special=w.num_special, grid_h=w.grid_h,
-                              grid_w=w.grid_w, rope_theta=w.rope_theta, max_frames=w.n_frames)
+                              grid_w=w.grid_w, rope_theta=w.rope_theta, max_frames=w.n_frames,
+                              window=w.infer_window, overlap=w.infer_overlap)
     c = oracle.OracleCache(cfg)
     # sampled frames: one early, one once the window has filled (at most the stream's end)
     fb = min(w.n_frames - 1, (w.A + w.W + 1) * w.keyframe_interval)
@@ -496,7 +497,9 @@ def stream_line(w, steps, warmup, cpu: bool):
         "ms_per_step": round(r["seconds"] * 1e3 / steps, 4),
         "config": {"tokens_per_frame": w.T, "heads": w.H, "head_dim": w.D, "page_size": w.P,
                    "frames_per_step": w.n_frames, "anchor": w.A, "window": w.W, "compact": w.C,
-                   "keyframe_interval": w.keyframe_interval, "drift_sigma": w.drift_sigma},
+                   "keyframe_interval": w.keyframe_interval, "drift_sigma": w.drift_sigma,
+                   **({"infer_window": w.infer_window, "infer_overlap": w.infer_overlap}
+                      if w.infer_window else {})},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(achieved / peak, 4)},
         "steady_state": {"frames": list(r["tail_frames"]), "value": round(r["tail_fps"], 2),
@@ -562,7 +565,8 @@ def main():
     if not args.stream_only and not args.no_configs and w is WL.FRAME1004_W16:
         # the long streams: fewer timed passes (each is 1,000 to 20,000 frames)
         line["configs"] = {}
-        for wl, st, wu in ((WL.STREAM1000_W64, 3, 1), (WL.STREAM10K_KF4, 1, 1), (WL.RING20K_W12, 1, 1)):
+        for wl, st, wu in ((WL.STREAM1000_W64, 3, 1), (WL.STREAM10K_KF4, 1, 1), (WL.RING20K_W12, 1, 1),
+                           (WL.WINDOWED1200, 2, 1)):
             sub, _ = stream_line(wl, st, wu, cpu=cpu)
             line["configs"][wl.name] = sub
     if cpu:

@@ -95,9 +95,25 @@ typedef struct {
                                 table and the trajectory) */
   int32_t num_pages;         /* ring size N; 0: peak of a keyframe stream,
                                 A*ceil(T/P) + (W+1)*ceil(T/P) +
-                                ceil(C*max(0, max_frames-A-W)/P) */
+                                ceil(C*max(0, F-A-W)/P), F = max_frames, or
+                                min(max_frames, infer_window) when windowed */
   const int32_t* ring_init;  /* N distinct page ids giving the initial free order
                                 (copied); NULL: 0, 1, ..., N-1 */
+  /* Windowed inference ("LingBot-Map runs 10,000 frames on monocular video",
+   * section "Cloning and Installing"; the project summary's "Main features"
+   * table: past the frame range the video rotary embedding was trained on,
+   * the memory slides as fixed-size windows overlapping by a few keyframes).
+   * With infer_window > 0 a window spans infer_window frames from its origin
+   * and the temporal rotary position of a frame (keys and queries) is its
+   * index relative to that origin.  The first frame appended outside the
+   * window starts the next one: the cache is reset and the last
+   * infer_overlap keyframes that fit in one window with that frame are
+   * appended again, oldest first, from raw copies the library keeps (their
+   * positions now relative to the oldest of them, the new origin); then the
+   * frame itself.  Requires 1 <= infer_overlap <= min(16, A + W) and
+   * infer_overlap < infer_window.  0 (the default) disables it. */
+  int32_t infer_window;
+  int32_t infer_overlap;
 } gca_config;
 
 /* Host-side occupancy (no device access). */
@@ -115,6 +131,7 @@ typedef struct {
   int64_t last_frame;        /* last appended frame index, -1 if none */
   int32_t max_splits;        /* split-KV workspace depth */
   int32_t reserved;
+  int64_t window_origin;     /* windowed inference: frame index of temporal position 0 */
 } gca_info;
 
 /* Device state copied to host buffers by gca_export_state.  Inputs: host
@@ -154,7 +171,12 @@ int gca_cache_reset(gca_cache* cache, gca_stream_t stream);
  * Errors: INVALID_ARGUMENT (null/misaligned, frame_idx < 0); SEQUENCE (a TEMP
  * frame is pending, frame_idx not above the last appended one, or W+1 window
  * frames are live and gca_evict_compact is due); CAPACITY (frame_idx >=
- * max_frames); OUT_OF_PAGES. */
+ * max_frames); OUT_OF_PAGES.
+ * Windowed inference (infer_window > 0): K is rotated at frame_idx minus the
+ * window origin; a keyframe's raw K and V are also copied into the library's
+ * overlap store; a frame_idx outside the window first restarts the cache as
+ * gca_config describes (ring back to its initial order, the kept keyframes
+ * appended again, enqueued on `stream` before this frame's append). */
 int gca_append_frame(gca_cache* cache, int64_t frame_idx, const void* k, const void* v,
                      uint32_t flags, gca_stream_t stream);
 
@@ -169,7 +191,8 @@ int gca_append_frame(gca_cache* cache, int64_t frame_idx, const void* k, const v
  * Errors: INVALID_ARGUMENT (null/misaligned, first_frame < 0, n_frames < 1);
  * CAPACITY (n_frames > 16, or a frame index >= max_frames); SEQUENCE (as
  * gca_append_frame for any frame of the batch, including an eviction coming
- * due inside it); OUT_OF_PAGES. */
+ * due inside it, or in windowed inference a frame past the first one that
+ * would start the next window); OUT_OF_PAGES. */
 int gca_append_frames(gca_cache* cache, int64_t first_frame, int32_t n_frames, const void* k,
                       const void* v, gca_stream_t stream);
 
@@ -182,7 +205,8 @@ int gca_evict_compact(gca_cache* cache, gca_stream_t stream);
 
 /* compute_attention(global_idx, q_nhd): build the gather list (anchor pages,
  * window pages oldest to newest with the current frame last, trajectory
- * pages), rotate Q at frame_idx (rope = 1) and write, for every token n and
+ * pages), rotate Q at frame_idx (rope = 1; minus the window origin in
+ * windowed inference) and write, for every token n and
  * head h, out[n][h] = sum_i softmax_i(sm_scale * q'.k'_i) v_i over the n_ctx
  * context tokens (no other mask: the current frame sees all of its own
  * tokens) and, if lse != NULL, lse[n][h] = natural log of the softmax
@@ -256,9 +280,11 @@ int gca_step_static(gca_cache* cache, int64_t frame_idx, const void* k, const vo
  * this itself).  Errors: SEQUENCE (empty cache). */
 int gca_select(gca_cache* cache, gca_stream_t stream);
 
-/* y = rotary embedding of x ([T][H][D], cache dtype) at frame frame_idx, the
- * same arithmetic gca_append_frame applies to K and gca_attend to Q.
- * Errors: INVALID_ARGUMENT, UNSUPPORTED (rope = 0), CAPACITY. */
+/* y = rotary embedding of x ([T][H][D], cache dtype) at temporal position
+ * frame_idx, the same arithmetic gca_append_frame applies to K and gca_attend
+ * to Q (in windowed inference frame_idx is the window-relative position).
+ * Errors: INVALID_ARGUMENT, UNSUPPORTED (rope = 0), CAPACITY (frame_idx >=
+ * max_frames, or >= infer_window in windowed inference). */
 int gca_rope3d(gca_cache* cache, int64_t frame_idx, const void* x, void* y, gca_stream_t stream);
 
 /* Host-side occupancy; no device access. */

@@ -38,27 +38,36 @@ struct RopeTabs {
 };
 
 struct AppendArgs {
-  const void* k;
+  const void* k;  // [T][H][D], raw
   const void* v;
+  void* raw_k;    // non-null: the raw K and V are also copied here ([T][H][D])
+  void* raw_v;
   void* kpool;  // [N][H][P][D]
   void* vpool;  // [N][H][D][P]
   const int32_t* ring;
   int32_t* rec_pages;  // [slots][ppf]
   int64_t ring_pos;
-  int64_t frame;
+  int64_t tpos;        // temporal rotary position of the frame
   int N, slot, ppf, T, H, P;
   int rope;
   RopeTabs tabs;
 };
 
-// Several keyframes appended in one launch: frame j (0 <= j < n) reads its
-// inputs at k, v + j * T * H * D elements, pops ring positions ring_pos + j *
-// ppf onwards and fills record slot slot[j]; `a` holds frame 0's arguments.
+// Several frames appended in one launch: frame j (0 <= j < n) reads its
+// inputs at k[j], v[j] (copying them to rk[j], rv[j] when those are
+// non-null), is rotated at temporal position tpos[j], pops ring positions
+// ring_pos + j * ppf onwards and fills record slot slot[j]; `a` holds the
+// arguments common to all.
 constexpr int kMaxAppendBatch = 16;
 struct AppendBatch {
   AppendArgs a;
   int n;
   int slot[kMaxAppendBatch];
+  int64_t tpos[kMaxAppendBatch];
+  const void* k[kMaxAppendBatch];
+  const void* v[kMaxAppendBatch];
+  void* rk[kMaxAppendBatch];
+  void* rv[kMaxAppendBatch];
 };
 
 struct EvictArgs {
@@ -125,9 +134,9 @@ struct MergeArgs {
 __host__ __device__ inline int vslot(int s) { return (s & ~12) | ((s & 4) << 1) | ((s & 8) >> 1); }
 
 struct RopeArgs {
-  const void* x;  // [nf][T][H][D]: frames frame, frame + 1, ..., frame + nf - 1
+  const void* x;  // [nf][T][H][D]: temporal positions tpos, tpos + 1, ..., tpos + nf - 1
   void* y;
-  int64_t frame;
+  int64_t tpos;
   int nf;
   int T, H;
   int rotate;   // 0: y = x

@@ -124,7 +124,7 @@ __device__ inline void rope_chunk(const RopeArgs& a, size_t c) {
   int tok = row % a.T;
   Vec16<T> v;
   v.u = ((const uint4*)a.x)[c];
-  if (a.rotate) rotate_chunk<T>(v, a.tabs, a.frame + row / a.T, tok, part * EPC / 2);
+  if (a.rotate) rotate_chunk<T>(v, a.tabs, a.tpos + row / a.T, tok, part * EPC / 2);
   ((uint4*)a.y)[c] = v.u;
 }
 template <typename T>
@@ -167,7 +167,11 @@ __device__ inline void append_block(const AppendArgs& a, int i, int h) {
       size_t off = ((size_t)tok * a.H + h) * kHeadDim + part * EPC;
       kv.u = *(const uint4*)(K + off);
       vv.u = *(const uint4*)(V + off);
-      if (a.rope) rotate_chunk<T>(kv, a.tabs, a.frame, tok, part * EPC / 2);
+      if (a.raw_k) {
+        *(uint4*)((T*)a.raw_k + off) = kv.u;
+        *(uint4*)((T*)a.raw_v + off) = vv.u;
+      }
+      if (a.rope) rotate_chunk<T>(kv, a.tabs, a.tpos, tok, part * EPC / 2);
     }
     *(uint4*)(kp + (size_t)s * kHeadDim + part * EPC) = kv.u;
     *(uint4*)(lds + s * LP + part * EPC) = vv.u;
@@ -196,11 +200,12 @@ template <typename T>
 __global__ __launch_bounds__(256) void k_append_batch(AppendBatch b) {
   const int j = blockIdx.x / b.a.ppf, i = blockIdx.x - j * b.a.ppf;
   AppendArgs a = b.a;
-  const size_t fe = (size_t)a.T * a.H * kHeadDim;
-  a.k = (const T*)b.a.k + j * fe;
-  a.v = (const T*)b.a.v + j * fe;
-  a.ring_pos = b.a.ring_pos + (int64_t)j * a.ppf;
-  a.frame = b.a.frame + j;
+  a.k = b.k[j];
+  a.v = b.v[j];
+  a.raw_k = b.rk[j];
+  a.raw_v = b.rv[j];
+  a.ring_pos = (b.a.ring_pos + (int64_t)j * a.ppf) % a.N;
+  a.tpos = b.tpos[j];
   a.slot = b.slot[j];
   append_block<T>(a, i, blockIdx.y);
 }

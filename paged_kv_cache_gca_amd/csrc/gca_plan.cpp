@@ -27,6 +27,11 @@ int make_geometry(const gca_config* c, Geometry* g) {
       return GCA_ERR_INVALID_ARGUMENT;
   }
   if (!std::isfinite(c->sm_scale) || !(c->sm_scale > 0.f)) return GCA_ERR_INVALID_ARGUMENT;
+  if (c->infer_window < 0 || c->infer_overlap < 0) return GCA_ERR_INVALID_ARGUMENT;
+  if (c->infer_window > 0 &&
+      (c->infer_overlap < 1 || c->infer_overlap > kMaxOverlap ||
+       c->infer_overlap > c->num_anchor_frames + c->window_frames || c->infer_overlap >= c->infer_window))
+    return GCA_ERR_INVALID_ARGUMENT;
   if (c->head_dim != 64) return GCA_ERR_UNSUPPORTED;
   if (c->page_size != 16 && c->page_size != 32 && c->page_size != 64) return GCA_ERR_UNSUPPORTED;
 
@@ -37,6 +42,9 @@ int make_geometry(const gca_config* c, Geometry* g) {
   o.num_special = c->num_special; o.grid_h = c->grid_h; o.grid_w = c->grid_w;
   o.rope = c->rope; o.theta = c->rope_theta; o.scale = c->sm_scale;
   o.max_frames = c->max_frames;
+  o.window = c->infer_window;
+  o.overlap = c->infer_window > 0 ? c->infer_overlap : 0;
+  o.rope_pos = o.window > 0 ? std::min<int64_t>(o.max_frames, o.window) : o.max_frames;
   o.ppf = (o.T + o.P - 1) / o.P;
   o.last_len = o.T - (o.ppf - 1) * o.P;
   o.Wr = o.W + 1;
@@ -61,7 +69,8 @@ int make_geometry(const gca_config* c, Geometry* g) {
       o.compact[s + j] = o.num_special + (int)(((int64_t)j * npatch) / rest);
   }
 
-  int64_t evictions = std::max<int64_t>(0, o.max_frames - o.A - o.W);
+  // at most one window's frames are cached between the resets of windowed inference
+  int64_t evictions = std::max<int64_t>(0, o.rope_pos - o.A - o.W);
   int64_t traj_pages = ((int64_t)o.C * evictions + o.P - 1) / o.P;
   int64_t n = c->num_pages > 0
                   ? (int64_t)c->num_pages
@@ -99,6 +108,57 @@ void Planner::reset() {
   traj_len_ = 0;
   n_traj_pages_ = 0;
   slot_frame_.assign(g_.A + g_.Wr, -1);
+  origin_ = 0;
+  raw_next_ = 0;
+  ov_frame_.clear();
+  ov_slot_.clear();
+}
+
+bool Planner::restart_due(int64_t frame) const {
+  return g_.window > 0 && has_last_ && frame >= 0 && frame - origin_ >= g_.window;
+}
+
+// The next window before frame `frame`: the last keyframes (at most
+// `overlap`, oldest first) that fit in one window with it, re-appended into a
+// freshly reset cache at positions relative to the oldest of them.
+int Planner::check_restart(int64_t frame, RestartStep* out) const {
+  if (temp_) return GCA_ERR_SEQUENCE;
+  if (frame <= last_) return GCA_ERR_SEQUENCE;
+  if (frame >= g_.max_frames) return GCA_ERR_CAPACITY;
+  out->n = 0;
+  out->origin = frame;
+  for (size_t i = 0; i < ov_frame_.size(); ++i)
+    if (frame - ov_frame_[i] < g_.window) {
+      if (out->n == 0) out->origin = ov_frame_[i];
+      AppendStep& a = out->step[out->n++];
+      a.frame = ov_frame_[i];
+      a.raw_slot = ov_slot_[i];
+    }
+  // a fresh cache: ring from its initial order, anchors first
+  for (int j = 0; j < out->n; ++j) {
+    AppendStep& a = out->step[j];
+    a.rope = a.frame - out->origin;
+    a.ring_pos = (int64_t)j * g_.ppf;
+    a.slot = j < g_.A ? j : g_.A + (j - g_.A) % g_.Wr;
+  }
+  if ((int64_t)out->n * g_.ppf > g_.N) return GCA_ERR_OUT_OF_PAGES;
+  return GCA_OK;
+}
+
+void Planner::commit_restart(const RestartStep& r) {
+  std::vector<int64_t> fr;
+  std::vector<int> sl;
+  for (int j = 0; j < r.n; ++j) {
+    fr.push_back(r.step[j].frame);
+    sl.push_back(r.step[j].raw_slot);
+  }
+  const int64_t rn = raw_next_;
+  reset();
+  raw_next_ = rn;
+  for (int j = 0; j < r.n; ++j) place(r.step[j], false);
+  origin_ = r.origin;
+  ov_frame_ = fr;
+  ov_slot_ = sl;
 }
 
 int Planner::check_append(int64_t frame, bool temp, AppendStep* out) const {
@@ -109,13 +169,32 @@ int Planner::check_append(int64_t frame, bool temp, AppendStep* out) const {
   if (!anchor && win_count_ >= g_.Wr) return GCA_ERR_SEQUENCE;  // eviction is due
   if (frame >= g_.max_frames) return GCA_ERR_CAPACITY;
   if (tail_ - head_ < g_.ppf) return GCA_ERR_OUT_OF_PAGES;
+  // windowed inference: a frame outside the window needs the restart first
+  if (g_.window > 0 && has_last_ && frame - origin_ >= g_.window) return GCA_ERR_SEQUENCE;
   out->frame = frame;
+  out->rope = g_.window > 0 ? (has_last_ ? frame - origin_ : 0) : frame;
   out->ring_pos = head_;
   out->slot = anchor ? n_anchor_ : g_.A + (win_first_ + win_count_) % g_.Wr;
+  out->raw_slot = g_.window > 0 && !temp ? (int)(raw_next_ % g_.overlap) : -1;
   return GCA_OK;
 }
 
 void Planner::commit_append(const AppendStep& s, bool temp) {
+  place(s, temp);
+  if (g_.window > 0 && !temp) {
+    // a keyframe appended by the caller: its raw copy went to the next raw slot
+    raw_next_++;
+    ov_frame_.push_back(s.frame);
+    ov_slot_.push_back(s.raw_slot);
+    if ((int)ov_frame_.size() > g_.overlap) {
+      ov_frame_.erase(ov_frame_.begin());
+      ov_slot_.erase(ov_slot_.begin());
+    }
+  }
+}
+
+void Planner::place(const AppendStep& s, bool temp) {
+  if (g_.window > 0 && !has_last_) origin_ = s.frame;  // the first frame opens the first window
   head_ += g_.ppf;
   slot_frame_[s.slot] = s.frame;
   if (s.slot < g_.A) n_anchor_++;
@@ -210,6 +289,7 @@ void Planner::info(gca_info* o) const {
   o->last_frame = has_last_ ? last_ : -1;
   o->max_splits = 0;
   o->reserved = 0;
+  o->window_origin = g_.window > 0 ? origin_ : 0;
 }
 
 void Planner::live_frames(std::vector<int>* slots, std::vector<int64_t>* frames) const {
@@ -262,9 +342,16 @@ int gca_plan_append(gca_plan* plan, int64_t frame_idx, uint32_t flags) {
   if (!plan || (flags & ~GCA_APPEND_TEMP)) return GCA_ERR_INVALID_ARGUMENT;
   gca::AppendStep s;
   bool temp = flags & GCA_APPEND_TEMP;
-  int rc = plan->p.check_append(frame_idx, temp, &s);
-  if (rc) return rc;
-  plan->p.commit_append(s, temp);
+  gca::Planner p = plan->p;
+  int rc;
+  if (p.restart_due(frame_idx)) {
+    gca::RestartStep r;
+    if ((rc = p.check_restart(frame_idx, &r))) return rc;
+    p.commit_restart(r);
+  }
+  if ((rc = p.check_append(frame_idx, temp, &s))) return rc;
+  p.commit_append(s, temp);
+  plan->p = p;
   return GCA_OK;
 }
 

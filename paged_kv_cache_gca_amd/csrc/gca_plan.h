@@ -28,6 +28,9 @@ struct Geometry {
   int64_t max_frames;
   int ppf;          // pages per frame = ceil(T / P)
   int N;            // ring size
+  int window;       // windowed inference: frames per window (0 = off)
+  int overlap;      // keyframes carried into the next window
+  int64_t rope_pos; // temporal rotary positions in the table
   int Wr;           // window record slots = W + 1
   int traj_cap;     // trajectory page capacity
   int sel_cap;      // gather-list capacity
@@ -40,8 +43,19 @@ int make_geometry(const gca_config* cfg, Geometry* g);
 // Launch parameters of one append.
 struct AppendStep {
   int64_t frame;
+  int64_t rope;      // temporal rotary position (window-relative when windowed)
   int64_t ring_pos;  // ring counter of the first popped page
   int slot;          // record slot receiving the frame's pages
+  int raw_slot;      // windowed keyframe: its raw-copy slot, else -1
+};
+
+// Windowed inference: the start of the next window, before appending frame
+// `frame`: reset, then these keyframes appended again from their raw copies.
+constexpr int kMaxOverlap = 16;
+struct RestartStep {
+  int64_t origin;
+  int n;
+  AppendStep step[kMaxOverlap];  // raw_slot: where each one's raw copy is
 };
 
 // Launch parameters of one eviction.
@@ -70,6 +84,11 @@ class Planner {
   void reset();
 
   // Each check_* validates without changing state; commit_* applies it.
+  // Windowed inference: whether appending `frame` starts the next window,
+  // and that restart (call before check_append of the frame).
+  bool restart_due(int64_t frame) const;
+  int check_restart(int64_t frame, RestartStep* out) const;
+  void commit_restart(const RestartStep& r);
   int check_append(int64_t frame, bool temp, AppendStep* out) const;
   void commit_append(const AppendStep& s, bool temp);
   int check_evict(std::vector<EvictStep>* out) const;
@@ -83,11 +102,17 @@ class Planner {
   // Record slots of the live frames in gather order and their frame indices.
   void live_frames(std::vector<int>* slots, std::vector<int64_t>* frames) const;
   int64_t ring_head() const { return head_; }
+  int64_t origin() const { return origin_; }
+  // temporal rotary position of frame index f
+  int64_t rope_of(int64_t f) const { return g_.window > 0 ? f - origin_ : f; }
   int64_t ring_tail() const { return tail_; }
   bool empty() const { return n_anchor_ + win_count_ == 0; }
   const Geometry& geometry() const { return g_; }
 
  private:
+  // the page and slot bookkeeping of an append
+  void place(const AppendStep& s, bool temp);
+
   Geometry g_;
   int64_t head_ = 0, tail_ = 0;  // ring counters; slot = counter mod N
   int n_anchor_ = 0;
@@ -98,6 +123,11 @@ class Planner {
   int64_t traj_len_ = 0;
   int n_traj_pages_ = 0;
   std::vector<int64_t> slot_frame_;  // frame index held by each record slot
+  // windowed inference
+  int64_t origin_ = 0;
+  int64_t raw_next_ = 0;                // raw-copy slot of the next keyframe: raw_next_ % overlap
+  std::vector<int64_t> ov_frame_;       // the window's last keyframes, oldest first ...
+  std::vector<int> ov_slot_;            // ... and their raw-copy slots
 };
 
 }  // namespace gca

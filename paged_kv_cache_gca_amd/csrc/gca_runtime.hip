@@ -92,6 +92,8 @@ struct gca_cache {
   void* vpool = nullptr;
   int32_t* ring = nullptr;
   int32_t* ring_init = nullptr;  // device copy of a caller order, or null
+  void* raw_k = nullptr;  // windowed inference: raw K/V of the last keyframes, [overlap][T][H][D]
+  void* raw_v = nullptr;
   int32_t* rec_pages = nullptr;
   int32_t* traj_pages = nullptr;
   int32_t* compact = nullptr;
@@ -122,7 +124,7 @@ struct gca_cache {
 namespace {
 
 void free_all(gca_cache* c) {
-  void* ptrs[] = {c->kpool, c->vpool, c->ring, c->ring_init, c->rec_pages, c->traj_pages,
+  void* ptrs[] = {c->kpool, c->vpool, c->ring, c->ring_init, c->raw_k, c->raw_v, c->rec_pages, c->traj_pages,
                   c->compact, c->sel_page, c->sel_len, c->rope_t, c->rope_h, c->rope_w,
                   c->o_part, c->lse_part, c->qrot};
   for (void* p : ptrs)
@@ -157,7 +159,7 @@ void build_rope(const gca::Geometry& g, std::vector<double2>* t, std::vector<dou
         (*out)[(size_t)p * npairs + j] = make_double2(std::cos(ang), std::sin(ang));
       }
   };
-  fill(t, g.max_frames, dt);
+  fill(t, g.rope_pos, dt);
   fill(h, g.grid_h, dh);
   fill(w, g.grid_w, dw);
 }
@@ -216,16 +218,20 @@ gca::SelectArgs select_args(gca_cache* c, const gca::SelectStep& st) {
   return a;
 }
 
+size_t frame_bytes(const gca_cache* c) { return (size_t)c->g.T * c->g.H * c->g.D * c->esize; }
+
 gca::AppendArgs append_args(gca_cache* c, const gca::AppendStep& st, const void* k, const void* v) {
   gca::AppendArgs a;
   a.k = k;
   a.v = v;
+  a.raw_k = st.raw_slot >= 0 ? (char*)c->raw_k + st.raw_slot * frame_bytes(c) : nullptr;
+  a.raw_v = st.raw_slot >= 0 ? (char*)c->raw_v + st.raw_slot * frame_bytes(c) : nullptr;
   a.kpool = c->kpool;
   a.vpool = c->vpool;
   a.ring = c->ring;
   a.rec_pages = c->rec_pages;
   a.ring_pos = st.ring_pos % c->g.N;
-  a.frame = st.frame;
+  a.tpos = st.rope;
   a.N = c->g.N;
   a.slot = st.slot;
   a.ppf = c->g.ppf;
@@ -260,12 +266,13 @@ gca::EvictArgs evict_args(gca_cache* c, const gca::EvictStep& st) {
 }
 
 // The attention's queries: rotated when rope = 1 (rounded once to the cache
-// dtype), else copied, into the query workspace.
-gca::RopeArgs query_args(gca_cache* c, int64_t frame_idx, const void* q, void* dst, int nf = 1) {
+// dtype) at temporal position tpos (the frame index, window-relative in
+// windowed inference), else copied, into the query workspace.
+gca::RopeArgs query_args(gca_cache* c, int64_t tpos, const void* q, void* dst, int nf = 1) {
   gca::RopeArgs ra;
   ra.x = q;
   ra.y = dst;
-  ra.frame = frame_idx;
+  ra.tpos = tpos;
   ra.nf = nf;
   ra.T = c->g.T;
   ra.H = c->g.H;
@@ -386,6 +393,40 @@ int attend_launch(gca_cache* c, int64_t frame_idx, void* out, float* lse, const 
   return GCA_OK;
 }
 
+// Windowed inference: the start of the next window on the device.  The ring
+// back in its initial order, then the kept keyframes appended again from
+// their raw copies in one launch.
+int enqueue_restart(gca_cache* c, const gca::RestartStep& r, hipStream_t s) {
+  Prof p(c, 0, s);
+  GCA_HIP(gca::launch_ring_init(c->ring, c->ring_init, c->g.N, s), "ring init launch");
+  if (r.n == 0) return GCA_OK;
+  gca::AppendBatch b{};
+  b.a = append_args(c, r.step[0], nullptr, nullptr);
+  b.a.raw_k = b.a.raw_v = nullptr;
+  b.n = r.n;
+  for (int j = 0; j < r.n; ++j) {
+    const gca::AppendStep& st = r.step[j];
+    b.slot[j] = st.slot;
+    b.tpos[j] = st.rope;
+    b.k[j] = (const char*)c->raw_k + st.raw_slot * frame_bytes(c);
+    b.v[j] = (const char*)c->raw_v + st.raw_slot * frame_bytes(c);
+    b.rk[j] = b.rv[j] = nullptr;
+  }
+  GCA_HIP(gca::launch_append_batch(c->g.dtype, b, s), "append kernel launch");
+  return GCA_OK;
+}
+
+// On planner p: the restart due before appending `frame`, if any (r->n = -1
+// when none).
+int plan_restart(gca::Planner& p, int64_t frame, gca::RestartStep* r) {
+  r->n = -1;
+  if (!p.restart_due(frame)) return GCA_OK;
+  int rc = p.check_restart(frame, r);
+  if (rc) return rc;
+  p.commit_restart(*r);
+  return GCA_OK;
+}
+
 int do_select(gca_cache* c, hipStream_t s, gca::SelectStep* out) {
   gca::SelectStep st = c->plan.select();
   gca::SelectArgs a = select_args(c, st);
@@ -455,6 +496,11 @@ int gca_cache_create(const gca_config* cfg, gca_cache** out) {
   // prepared queries: one frame, or the A anchor frames of a joint call
   if ((e = dmalloc(&c->qrot, rows * g.D * c->esize * std::max(1, g.A))) != hipSuccess)
     return fail(e, "hipMalloc query workspace");
+  if (g.window > 0) {
+    const size_t rb = (size_t)g.overlap * rows * g.D * c->esize;
+    if ((e = dmalloc(&c->raw_k, rb)) != hipSuccess) return fail(e, "hipMalloc raw keyframes");
+    if ((e = dmalloc(&c->raw_v, rb)) != hipSuccess) return fail(e, "hipMalloc raw keyframes");
+  }
   if ((e = hipMemset(c->kpool, 0, pool_bytes)) != hipSuccess) return fail(e, "hipMemset K pool");
   if ((e = hipMemset(c->vpool, 0, pool_bytes)) != hipSuccess) return fail(e, "hipMemset V pool");
   if (g.C) {
@@ -525,16 +571,21 @@ int gca_append_frame(gca_cache* c, int64_t frame_idx, const void* k, const void*
   if (!c || !aligned16(k) || !aligned16(v) || (flags & ~GCA_APPEND_TEMP))
     return GCA_ERR_INVALID_ARGUMENT;
   bool temp = flags & GCA_APPEND_TEMP;
-  gca::AppendStep st;
-  int rc = c->plan.check_append(frame_idx, temp, &st);
+  gca::Planner p = c->plan;
+  gca::RestartStep r;
+  int rc = plan_restart(p, frame_idx, &r);
   if (rc) return rc;
+  gca::AppendStep st;
+  if ((rc = p.check_append(frame_idx, temp, &st))) return rc;
+  p.commit_append(st, temp);
   hipStream_t s = (hipStream_t)stream;
+  if (r.n >= 0 && (rc = enqueue_restart(c, r, s))) return rc;
   gca::AppendArgs a = append_args(c, st, k, v);
   {
-    Prof p(c, 0, s);
+    Prof pr(c, 0, s);
     GCA_HIP(gca::launch_append(c->g.dtype, a, s), "append kernel launch");
   }
-  c->plan.commit_append(st, temp);
+  c->plan = p;
   c->sel_valid = false;
   return GCA_OK;
 }
@@ -547,23 +598,35 @@ int gca_append_frames(gca_cache* c, int64_t first_frame, int32_t n_frames, const
   // every append on a copy of the planner first, as the individual calls
   // would run them; nothing is enqueued or changed unless all are valid
   gca::Planner p = c->plan;
+  gca::RestartStep r;
+  int rc = plan_restart(p, first_frame, &r);
+  if (rc) return rc;
   gca::AppendBatch b{};
   int64_t pos0 = 0;
+  const size_t fb = frame_bytes(c);
   for (int j = 0; j < n_frames; ++j) {
     gca::AppendStep st;
-    int rc = p.check_append(first_frame + j, false, &st);
-    if (rc) return rc;
+    // windowed inference: a batch does not cross into the next window
+    if (j > 0 && p.restart_due(first_frame + j)) return GCA_ERR_SEQUENCE;
+    if ((rc = p.check_append(first_frame + j, false, &st))) return rc;
+    const gca::AppendArgs aj = append_args(c, st, (const char*)k + j * fb, (const char*)v + j * fb);
     if (j == 0) {
-      b.a = append_args(c, st, k, v);
+      b.a = aj;
       pos0 = st.ring_pos;
     } else if (st.ring_pos != pos0 + (int64_t)j * c->g.ppf) {
       return GCA_ERR_SEQUENCE;  // not reached: with no eviction between them the pops are consecutive
     }
     b.slot[j] = st.slot;
+    b.tpos[j] = aj.tpos;
+    b.k[j] = aj.k;
+    b.v[j] = aj.v;
+    b.rk[j] = aj.raw_k;
+    b.rv[j] = aj.raw_v;
     p.commit_append(st, false);
   }
   b.n = n_frames;
   hipStream_t s = (hipStream_t)stream;
+  if (r.n >= 0 && (rc = enqueue_restart(c, r, s))) return rc;
   {
     Prof pr(c, 0, s);
     GCA_HIP(gca::launch_append_batch(c->g.dtype, b, s), "append kernel launch");
@@ -607,7 +670,8 @@ int gca_attend(gca_cache* c, int64_t frame_idx, const void* q, void* out, float*
   {
     // gather list and prepared queries from one launch
     Prof p(c, 2, s);
-    GCA_HIP(gca::launch_prepare(g.dtype, select_args(c, st), query_args(c, frame_idx, q, c->qrot), s),
+    GCA_HIP(gca::launch_prepare(g.dtype, select_args(c, st),
+                                query_args(c, c->plan.rope_of(frame_idx), q, c->qrot), s),
             "prepare kernel launch");
   }
   c->sel_valid = true;
@@ -629,8 +693,8 @@ int gca_attend_frames(gca_cache* c, int64_t first_frame, int32_t n_frames, const
   gca::SelectStep st = c->plan.select();
   {
     Prof p(c, 2, s);
-    GCA_HIP(gca::launch_prepare(g.dtype, select_args(c, st), query_args(c, first_frame, q, c->qrot, n_frames),
-                                s),
+    GCA_HIP(gca::launch_prepare(g.dtype, select_args(c, st),
+                                query_args(c, c->plan.rope_of(first_frame), q, c->qrot, n_frames), s),
             "prepare kernel launch");
   }
   c->sel_valid = true;
@@ -667,9 +731,11 @@ int step_impl(gca_cache* c, int64_t frame_idx, const void* k, const void* v, con
   // the whole step on a copy of the planner first: nothing is enqueued or
   // changed unless every part is valid
   gca::Planner p = c->plan;
-  gca::AppendStep as;
-  int rc = p.check_append(frame_idx, !key, &as);
+  gca::RestartStep rs;
+  int rc = plan_restart(p, frame_idx, &rs);
   if (rc) return rc;
+  gca::AppendStep as;
+  if ((rc = p.check_append(frame_idx, !key, &as))) return rc;
   p.commit_append(as, !key);
   std::vector<gca::EvictStep> ev;
   if (key) {
@@ -702,7 +768,8 @@ int step_impl(gca_cache* c, int64_t frame_idx, const void* k, const void* v, con
     const gca::SelectStep st2 = c->plan.select();
     {
       Prof pr(c, 2, s);
-      GCA_HIP(gca::launch_prepare(g.dtype, select_args(c, st2), query_args(c, frame_idx, q, w.qrot), s),
+      GCA_HIP(gca::launch_prepare(g.dtype, select_args(c, st2),
+                                  query_args(c, c->plan.rope_of(frame_idx), q, w.qrot), s),
               "prepare kernel launch");
     }
     c->sel_valid = true;
@@ -710,10 +777,11 @@ int step_impl(gca_cache* c, int64_t frame_idx, const void* k, const void* v, con
     c->sel_ctx = st2.n_ctx;
     return attend_launch(c, frame_idx, out, lse, st2, s, w);
   }
+  if (rs.n >= 0 && (rc = enqueue_restart(c, rs, s))) return rc;
   gca::AppendArgs aa = append_args(c, as, k, v);
   gca::EvictArgs ea{};
   if (!ev.empty()) ea = evict_args(c, ev[0]);
-  gca::RopeArgs ra = query_args(c, frame_idx, q, w.qrot);
+  gca::RopeArgs ra = query_args(c, p.rope_of(frame_idx), q, w.qrot);
   gca::SelectArgs sa = select_args(c, st);
   sa.newest_pos = as.ring_pos % g.N;
   if (!ev.empty()) {
@@ -755,12 +823,12 @@ int gca_step_static(gca_cache* c, int64_t frame_idx, const void* k, const void* 
 int gca_rope3d(gca_cache* c, int64_t frame_idx, const void* x, void* y, gca_stream_t stream) {
   if (!c || !aligned16(x) || !aligned16(y) || frame_idx < 0) return GCA_ERR_INVALID_ARGUMENT;
   if (!c->g.rope) return GCA_ERR_UNSUPPORTED;
-  if (frame_idx >= c->g.max_frames) return GCA_ERR_CAPACITY;
+  if (frame_idx >= c->g.rope_pos) return GCA_ERR_CAPACITY;
   hipStream_t s = (hipStream_t)stream;
   gca::RopeArgs a;
   a.x = x;
   a.y = y;
-  a.frame = frame_idx;
+  a.tpos = frame_idx;
   a.nf = 1;
   a.T = c->g.T;
   a.H = c->g.H;

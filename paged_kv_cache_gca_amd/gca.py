@@ -44,6 +44,7 @@ class gca_config(C.Structure):
         ("rope", C.c_int32), ("rope_theta", C.c_float), ("sm_scale", C.c_float),
         ("max_frames", C.c_int64), ("num_pages", C.c_int32),
         ("ring_init", C.POINTER(C.c_int32)),
+        ("infer_window", C.c_int32), ("infer_overlap", C.c_int32),
     ]
 
 
@@ -53,7 +54,7 @@ class gca_info(C.Structure):
         ("anchor_frames", C.c_int32), ("window_frames", C.c_int32), ("temp_pending", C.c_int32),
         ("traj_pages", C.c_int32), ("n_sel", C.c_int32), ("traj_tokens", C.c_int64),
         ("n_ctx", C.c_int64), ("last_frame", C.c_int64), ("max_splits", C.c_int32),
-        ("reserved", C.c_int32),
+        ("reserved", C.c_int32), ("window_origin", C.c_int64),
     ]
 
 
@@ -155,6 +156,8 @@ class Config:
     max_frames: int = 64
     num_pages: int = 0
     ring_init: list | None = None
+    infer_window: int = 0   # windowed inference: frames per window (0 = off)
+    infer_overlap: int = 0  # keyframes carried into the next window
 
     def to_c(self):
         keep = []
@@ -178,6 +181,7 @@ class Config:
             arr = (C.c_int32 * len(self.ring_init))(*self.ring_init)
             keep.append(arr)
             c.ring_init = C.cast(arr, C.POINTER(C.c_int32))
+        c.infer_window, c.infer_overlap = self.infer_window, self.infer_overlap
         return c, keep
 
     @staticmethod
@@ -185,7 +189,7 @@ class Config:
         d = dict(tokens_per_frame=w.T, num_heads=w.H, head_dim=w.D, page_size=w.P, dtype=w.dtype,
                  num_anchor_frames=w.A, window_frames=w.W, num_compact=w.C, rope=w.rope,
                  num_special=w.num_special, grid_h=w.grid_h, grid_w=w.grid_w, rope_theta=w.rope_theta,
-                 max_frames=w.n_frames)
+                 max_frames=w.n_frames, infer_window=w.infer_window, infer_overlap=w.infer_overlap)
         d.update(kw)
         return Config(**d)
 

@@ -5,7 +5,9 @@ plus 5 special tokens, i.e. 1004 tokens per frame; the global attention uses
 16 heads of width 64 (embed_dim 1024).  Stream lengths, window sizes and
 keyframe intervals follow the runs the pages describe: 1,000-frame sequences
 with a 64-frame window, 10,000-frame streams with keyframe-only caching, and
-a strict 12-frame sliding window (current frame + 11 cached frames).
+a strict 12-frame sliding window (current frame + 11 cached frames), and
+windowed inference past the video rotary range (windows of 128 frames
+overlapping by 8 keyframes).
 
 Only parameters live here; no arithmetic of the method.
 """
@@ -35,6 +37,8 @@ class Workload:
     drift_sigma: float = 0.0
     seed: int = 1
     rope_theta: float = 10000.0
+    infer_window: int = 0          # windowed inference: frames per window (0 = off)
+    infer_overlap: int = 0         # keyframes carried into the next window
 
     @property
     def n_keyframes(self) -> int:
@@ -71,4 +75,24 @@ CAMERA_T1 = Workload("bf16_T1_H16_P16_W32_camera_1000f", T=1, H=16, D=64, P=16, 
                      n_frames=1000, A=1, W=32, C=1, rope=1, num_special=0, grid_h=1, grid_w=1,
                      n_base=64, seed=6, rope_theta=100.0)
 
-ALL = [TINY_F32, FRAME1004_W16, STREAM1000_W64, STREAM10K_KF4, RING20K_W12, CAMERA_T1]
+# Windowed inference: windows of 128 frames overlapping by 8 keyframes, the
+# documented setting for streams past the 320 views the video rotary embedding
+# was trained on; every second frame a keyframe.
+WINDOWED1200 = Workload("bf16_T1004_H16_P64_W32_win128_ov8_1200f_kf2", T=1004, H=16, D=64, P=64,
+                        dtype="bf16", n_frames=1200, A=1, W=32, C=13, rope=1, num_special=5,
+                        grid_h=27, grid_w=37, keyframe_interval=2, n_base=64, seed=7,
+                        infer_window=128, infer_overlap=8)
+
+# Small windowed streams: every third frame a keyframe, so that the oldest
+# overlap keyframe sometimes falls outside the next window (f32), and every
+# frame a keyframe with a ragged last page (bf16).
+WINDOWED_SMALL_F32 = Workload("f32_T66_H2_P16_W3_win8_ov3_40f_kf3", T=66, H=2, D=64, P=16,
+                              dtype="f32", n_frames=40, A=1, W=3, C=3, rope=1, num_special=2,
+                              grid_h=8, grid_w=8, keyframe_interval=3, seed=8,
+                              infer_window=8, infer_overlap=3)
+WINDOWED_SMALL_BF16 = Workload("bf16_T70_H2_P32_W2_win6_ov2_30f", T=70, H=2, D=64, P=32,
+                               dtype="bf16", n_frames=30, A=1, W=2, C=5, rope=1, num_special=6,
+                               grid_h=8, grid_w=8, seed=9, infer_window=6, infer_overlap=2)
+
+ALL = [TINY_F32, FRAME1004_W16, STREAM1000_W64, STREAM10K_KF4, RING20K_W12, CAMERA_T1,
+       WINDOWED1200, WINDOWED_SMALL_F32, WINDOWED_SMALL_BF16]

@@ -33,7 +33,7 @@ def stream_of(w: WL.Workload) -> FrameStream:
 def oracle_cfg(w: WL.Workload, **kw) -> oracle.OracleConfig:
     d = dict(T=w.T, H=w.H, D=w.D, P=w.P, dtype=w.dtype, A=w.A, W=w.W, C=w.C, rope=w.rope,
              num_special=w.num_special, grid_h=w.grid_h, grid_w=w.grid_w, rope_theta=w.rope_theta,
-             max_frames=w.n_frames)
+             max_frames=w.n_frames, window=w.infer_window, overlap=w.infer_overlap)
     d.update(kw)
     return oracle.OracleConfig(**d)
 

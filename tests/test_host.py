@@ -68,6 +68,27 @@ def test_plan_rejects_bad_configs(field, value, code):
     assert ei.value.code == code
 
 
+@pytest.mark.parametrize("window,overlap,A,W,code", [
+    (8, 0, 1, 3, -1),     # a window needs at least one overlap keyframe
+    (8, 8, 4, 8, -1),     # overlap below the window
+    (8, 5, 1, 3, -1),     # at most A + W keyframes carried over
+    (40, 17, 8, 16, -1),  # at most 16 (one re-append launch)
+    (-1, 0, 1, 3, -1),
+    (8, 3, 1, 3, 0),
+    (40, 16, 8, 16, 0),
+])
+def test_plan_windowed_config_rules(window, overlap, A, W, code):
+    from paged_kv_cache_gca_amd import gca
+    c = cfg_of(WL.TINY_F32, infer_window=window, infer_overlap=overlap, num_anchor_frames=A,
+               window_frames=W)
+    if code:
+        with pytest.raises(gca.GCAError) as e:
+            gca.Plan(c)
+        assert e.value.code == code
+    else:
+        gca.Plan(c)
+
+
 def test_plan_rejects_rope_grid_mismatch_and_bad_ring():
     from paged_kv_cache_gca_amd import gca
     c = cfg_of(WL.FRAME1004_W16, grid_w=36)
@@ -136,7 +157,8 @@ def test_default_num_pages_matches_oracle_rule():
         p = gca.Plan(cfg_of(w))
         assert p.query().num_pages == oracle.default_num_pages(
             oracle.OracleConfig(T=w.T, H=w.H, D=w.D, P=w.P, A=w.A, W=w.W, C=w.C,
-                                max_frames=w.n_frames))
+                                max_frames=w.n_frames, window=w.infer_window,
+                                overlap=w.infer_overlap))
 
 
 @pytest.mark.parametrize("w", WL.ALL, ids=lambda w: w.name)
@@ -144,7 +166,8 @@ def test_plan_occupancy_matches_oracle_every_step(w):
     from paged_kv_cache_gca_amd import gca
     p = gca.Plan(cfg_of(w))
     o = oracle.OracleCache(oracle.OracleConfig(T=w.T, H=w.H, D=w.D, P=w.P, A=w.A, W=w.W, C=w.C,
-                                               num_special=w.num_special, max_frames=w.n_frames))
+                                               num_special=w.num_special, max_frames=w.n_frames,
+                                               window=w.infer_window, overlap=w.infer_overlap))
     n = min(w.n_frames, 3000)
     for f in range(n):
         key = w.is_keyframe(f)
@@ -155,6 +178,8 @@ def test_plan_occupancy_matches_oracle_every_step(w):
         assert p.attend(f) == 0
         info = p.query()
         assert info.n_ctx == o.n_ctx()
+        if w.infer_window:
+            assert info.window_origin == f - o.rope_position(f)
         if f % 97 == 0 or f == n - 1:
             page, ln, n_ctx = o.select()
             st = o.state()
