@@ -5,7 +5,9 @@
 // checked against the pool rules' closed form for the context size:
 //   n_ctx = A' T + w T + C e + (T if a non-keyframe is pending),
 // A' anchors so far, w window keyframes, e evictions.
+// Windowed inference is checked against a model of its window starts.
 // Exits non-zero on the first mismatch; a sanitizer report aborts the run.
+#include <algorithm>
 #include <cstdint>
 #include <cstdio>
 #include <random>
@@ -97,6 +99,57 @@ static void stream(const gca_config& cfg, int interval, uint64_t seed) {
   EXPECT(gca_plan_destroy(p) == GCA_OK);
 }
 
+// Windowed inference: a model of the window starts (the last `overlap`
+// keyframes that fit in a window with the new frame are kept, the oldest kept
+// one becomes the origin) checked against the planner's context size and
+// origin at every frame.
+static void windowed(gca_config cfg, int window, int overlap, int interval) {
+  cfg.infer_window = window;
+  cfg.infer_overlap = overlap;
+  gca_plan* p = nullptr;
+  EXPECT(gca_plan_create(&cfg, &p) == GCA_OK);
+  if (!p) return;
+  const int64_t T = cfg.tokens_per_frame;
+  const int A = cfg.num_anchor_frames, W = cfg.window_frames;
+  int64_t anchors = 0, win = 0, evictions = 0, origin = 0;
+  std::vector<int64_t> keys;  // the last `overlap` keyframes
+  int starts = 0;
+  for (int64_t f = 0; f < cfg.max_frames; ++f) {
+    const bool key = f % interval == 0;
+    if (f > 0 && f - origin >= window) {
+      std::vector<int64_t> kept;
+      for (int64_t k : keys)
+        if (f - k < window) kept.push_back(k);
+      keys = kept;
+      origin = kept.empty() ? f : kept.front();
+      anchors = std::min<int64_t>(A, (int64_t)kept.size());
+      win = (int64_t)kept.size() - anchors;
+      evictions = 0;
+      starts++;
+    }
+    EXPECT(gca_plan_append(p, f, key ? 0u : (uint32_t)GCA_APPEND_TEMP) == GCA_OK);
+    if (key) {
+      if (anchors < A) anchors++;
+      else win++;
+      keys.push_back(f);
+      if ((int)keys.size() > overlap) keys.erase(keys.begin());
+      EXPECT(gca_plan_evict(p) == GCA_OK);
+      while (win > W) {
+        win--;
+        evictions++;
+      }
+    }
+    EXPECT(gca_plan_attend(p, f) == GCA_OK);
+    gca_info inf;
+    EXPECT(gca_plan_query(p, &inf) == GCA_OK);
+    EXPECT(inf.n_ctx == (anchors + win + (key ? 0 : 1)) * T + (int64_t)cfg.num_compact * evictions);
+    EXPECT(inf.window_origin == origin);
+    if (!key) EXPECT(gca_plan_rollback(p, f) == GCA_OK);
+  }
+  EXPECT(starts > 0);
+  EXPECT(gca_plan_destroy(p) == GCA_OK);
+}
+
 int main() {
   // bad configs are refused without leaks
   gca_config bad = base(64, 2, 16, 1, 2, 1, 6);
@@ -117,6 +170,10 @@ int main() {
   stream(base(64, 2, 16, 1, 2, 1, 200), 2, 5);
   stream(base(1, 16, 16, 1, 32, 1, 300), 1, 6);
   stream(base(300, 4, 32, 3, 2, 7, 150), 3, 7);
+  windowed(base(1004, 16, 64, 1, 32, 13, 1200), 128, 8, 2);
+  windowed(base(66, 2, 16, 1, 3, 3, 200), 8, 3, 3);
+  windowed(base(70, 2, 32, 1, 2, 5, 200), 6, 2, 1);
+  windowed(base(64, 2, 16, 2, 3, 2, 300), 5, 4, 2);
   if (fails) {
     std::fprintf(stderr, "%d expectations failed\n", fails);
     return 1;
