@@ -365,7 +365,8 @@ __global__ void k_ring_init(int32_t* ring, const int32_t* init, int N) {
 // straight from the S^T accumulators as the B operand of O^T = V^T P^T; the
 // key order inside each 16-key chunk follows the accumulator layout, and the
 // V^T operand is read in the same order.  Row sums are dot products of the
-// same rounded P with ones, so sum(P) and P.V use identical weights.
+// same rounded P with ones, so sum(P) and P.V use identical weights (they
+// sum to one exactly, so an offset common to all V rows passes through).
 
 template <typename T>
 struct Mfma;
@@ -691,15 +692,6 @@ struct DmaLoader {
   }
 };
 
-// s_waitcnt on the vector-memory count only (vmcnt <= N, N < 16): bits 3:0
-// vmcnt, 6:4 expcnt (7: no wait), 11:8 lgkmcnt (15: no wait), 15:14 the high
-// vmcnt bits (0 here)
-template <int N>
-__device__ inline void wait_vmem() {
-  static_assert(N >= 0 && N < 16, "vmcnt immediate");
-  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
-}
-
 // Row sums of P from the same rounded values the P.V product uses (this
 // lane's keys only; the lane pair l, l ^ 32 covers the whole tile).
 __device__ inline float rowsum_add(float l, bf16x8 p) {
@@ -716,7 +708,15 @@ __device__ inline float rowsum_add(float l, bf16x8 p) {
   }
   return l;
 }
-__device__ inline float rowsum_add(float l, float p) { return l + p; }
+
+// s_waitcnt on the vector-memory count only (vmcnt <= N, N < 16): bits 3:0
+// vmcnt, 6:4 expcnt (7: no wait), 11:8 lgkmcnt (15: no wait), 15:14 the high
+// vmcnt bits (0 here)
+template <int N>
+__device__ inline void wait_vmem() {
+  static_assert(N >= 0 && N < 16, "vmcnt immediate");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+}
 
 // max over the two 32-lane halves of the wave
 __device__ inline float half_swap_max(float x) {
@@ -1043,7 +1043,9 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf(AttnArgs a) {
     ld.init(h, a.H, tid);
     const char* kp = (const char*)a.kpool;
     const char* vp = (const char*)a.vpool;
-    auto buf = [&](int t) __attribute__((always_inline)) { return lt + (t & 3) * BB; };
+    // buffer of the split's i-th tile (i counted from t0): with the tile
+    // loop unrolled four times every buffer offset is a constant
+    auto buf = [&](int i) __attribute__((always_inline)) { return lt + (i & 3) * BB; };
     // mask bits of a tile: bit kb set when key kb*32 + l32 is masked
     auto minfo = [&](const typename DL::Ids& x) __attribute__((always_inline)) {
       int r = 0;
@@ -1117,6 +1119,11 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf(AttnArgs a) {
           bf16x2 pr;
           pr[0] = (bf16)xe[0];
           pr[1] = (bf16)xe[1];
+          // the pack stays in this group (it would otherwise sink to the
+          // end of the step, past the sum check)
+          uint32_t u = __builtin_bit_cast(uint32_t, pr);
+          asm volatile("" : "+v"(u));
+          pr = __builtin_bit_cast(bf16x2, u);
           pS[ch][qb][2 * k] = pr[0];
           pS[ch][qb][2 * k + 1] = pr[1];
           ts[qb] = __builtin_amdgcn_fdot2_f32_bf16(pr, one, ts[qb], false);
@@ -1207,9 +1214,9 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf(AttnArgs a) {
     ready(idc);
     ready(idd);
     asm volatile("" ::: "memory");
-    ld.issue(kp, vp, ida, buf(t0), wave);
-    ld.issue(kp, vp, idb, buf(t0 + 1), wave);
-    ld.issue(kp, vp, idc, buf(t0 + 2), wave);
+    ld.issue(kp, vp, ida, buf(0), wave);
+    ld.issue(kp, vp, idb, buf(1), wave);
+    ld.issue(kp, vp, idc, buf(2), wave);
     // mask bits of tiles t, t + 1, t + 2 in bits 0-1, 2-3, 4-5
     int mr = minfo(ida) | minfo(idb) << 2 | minfo(idc) << 4;
     idb = idd;  // the ids of tile t0 + 3, used in the first period
@@ -1226,15 +1233,15 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf(AttnArgs a) {
 #pragma unroll
       for (int qb = 0; qb < NQB; ++qb) p1[ch][qb] = Frag{};  // the P.V of step 0 adds nothing
     float ts[NQB];
-    qk_raw(buf(t0), 0, mr & 3, s0);
+    qk_raw(buf(0), 0, mr & 3, s0);
 
     // one tile period; `use` holds the ids of tile t + 3, `next` receives those of t + 4
     auto period = [&](int i, typename DL::Ids& use, typename DL::Ids& next) __attribute__((always_inline)) {
       const int t = t0 + i;
       // step 2i: QK of block 1 of tile t, softmax of block 0 of tile t, P.V of
       // block 1 of tile t - 1 (of tile t with P = 0 in the first step)
-      step(buf(t), 1, mr & 3, buf(i > 0 ? t - 1 : t), 1, s1, s0, p0, p1, ts);
-      settle(buf(t), 0, mr & 3, s0, p0, ts);
+      step(buf(i), 1, mr & 3, buf(i > 0 ? i - 1 : i), 1, s1, s0, p0, p1, ts);
+      settle(buf(i), 0, mr & 3, s0, p0, ts);
       // tile t + 1 has landed; tile t - 1's buffer is free: ids of tile t + 4,
       // data of tile t + 3 (past the split's end they are read and unused)
       asm volatile("" ::: "memory");
@@ -1244,23 +1251,25 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf(AttnArgs a) {
       asm volatile("" ::: "memory");
       ready(use);
       ld.fetch(a, t + 4, next);
-      ld.issue(kp, vp, use, buf(t + 3), wave);
+      ld.issue(kp, vp, use, buf(i + 3), wave);
       mr |= minfo(use) << 6;
       asm volatile("" ::: "memory");
       // step 2i + 1: QK of block 0 of tile t + 1, softmax of block 1 of tile t,
       // P.V of block 0 of tile t
-      step(buf(t + 1), 0, (mr >> 2) & 3, buf(t), 0, s0, s1, p1, p0, ts);
-      settle(buf(t), 1, mr & 3, s1, p1, ts);
+      step(buf(i + 1), 0, (mr >> 2) & 3, buf(i), 0, s0, s1, p1, p0, ts);
+      settle(buf(i), 1, mr & 3, s1, p1, ts);
       mr >>= 2;
     };
     // after the prologue idb holds the ids of tile t0 + 3
-    for (int i = 0; i < n; i += 2) {
+    for (int i = 0; i < n; i += 4) {
       period(i, idb, ida);
       if (i + 1 < n) period(i + 1, ida, idb);
+      if (i + 2 < n) period(i + 2, idb, ida);
+      if (i + 3 < n) period(i + 3, ida, idb);
     }
     // the last block's P.V
     {
-      const char* vb = buf(t0 + n - 1);
+      const char* vb = buf(n - 1);
 #pragma unroll
       for (int ch = 0; ch < NCH; ++ch)
 #pragma unroll
