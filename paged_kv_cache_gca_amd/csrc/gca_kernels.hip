@@ -513,6 +513,25 @@ __device__ inline i32x4 load_lens(const int32_t* p) {
   return v;
 }
 
+// The same, for a wave-uniform address: scalar loads.
+template <int N>
+__device__ inline i32x4 load_uniform(const int32_t* p) {
+  typedef const __attribute__((address_space(4))) int32_t cint;
+  typedef const __attribute__((address_space(4))) i32x2 cint2;
+  typedef const __attribute__((address_space(4))) i32x4 cint4;
+  i32x4 v = {0, 0, 0, 0};
+  if constexpr (N == 4) {
+    v = *(cint4*)(const void*)p;
+  } else if constexpr (N == 2) {
+    const i32x2 u = *(cint2*)(const void*)p;
+    v.x = u.x;
+    v.y = u.y;
+  } else {
+    v.x = *(cint*)(const void*)p;
+  }
+  return v;
+}
+
 // element j of v (a per-lane index): straight-line selects, no divergent branches
 __device__ inline int pick(i32x4 v, int j) {
   int r = v.x;
@@ -636,10 +655,9 @@ struct DmaLoader {
   static constexpr int EPT = kKeysPerTile / P;
   static constexpr int KBYTES = kKeysPerTile * kHeadDim * 2;  // 8 KB, then V^T 8 KB
   static constexpr int BUF_BYTES = 2 * KBYTES;
-  static constexpr int NFETCH = 2;  // vector loads per fetch: the tile's page ids, its lengths
   static constexpr int NISSUE = 4;  // DMA loads per wave and tile
-  // the EPT page ids and lengths of a tile, as loaded (every lane loads the
-  // same 4 to 16 bytes); each lane picks its pieces' entries when it issues
+  // the EPT page ids and lengths of a tile: wave-uniform, in scalar
+  // registers; each lane picks its pieces' entries when it issues
   struct Ids {
     i32x4 pg, ln;
   };
@@ -667,9 +685,12 @@ struct DmaLoader {
     ent = (8 * c) / P;
     off = (uint32_t)((d * P + (8 * c) % P) * 2);
   }
+  // scalar loads through the constant address space (the gather list is
+  // not written during the launch): no vector registers, and nothing for the
+  // vector-memory counter, which then tracks the tile data alone
   __device__ void fetch(const AttnArgs& a, int tile, Ids& x) const {
-    x.pg = load_lens<EPT>(a.sel_page + tile * EPT);
-    x.ln = load_lens<EPT>(a.sel_len + tile * EPT);
+    x.pg = load_uniform<EPT>(a.sel_page + tile * EPT);
+    x.ln = load_uniform<EPT>(a.sel_len + tile * EPT);
   }
   __device__ void issue(const char* kpool, const char* vpool, const Ids& x, char* buf, int /*wave*/) const {
     typedef __attribute__((address_space(3))) void lds_t;
@@ -992,16 +1013,19 @@ __device__ inline void attn_epilogue_bf(const AttnArgs& a, const floatx16 (&o)[2
 // bf16 paged attention, software-pipelined over 32-key blocks.
 //
 // Workgroup shape, mapping and splits as in k_attn.  Step j of a wave issues,
-// independently of one another, the K.Q^T MFMAs of key block j + 1, the
+// independently of one another, the P.V MFMAs of key block j - 1, the
 // softmax of block j (scaling, exponentials, packing, row sums: VALU) and the
-// P.V MFMAs of block j - 1, interleaved one MFMA to six VALU instructions, so
-// that one wave alone keeps both pipes of its SIMD busy.  Block j's sums are
-// checked at the end of step j, before its P.V in step j + 1.  A 64-key tile
-// (two blocks) is read for its K from the step before its first block's
-// softmax and for its V^T until the step after its last one: two tiles are in
-// use, one is landing and a fourth buffer is being filled.  Tiles go straight
-// from memory into four LDS buffers (global_load_lds), issued three tiles
-// ahead, with one barrier per tile.
+// K.Q^T MFMAs of block j + 1, interleaved one MFMA to six VALU instructions,
+// so that the matrix and vector pipes of a SIMD stay busy together.  Every LDS
+// operand is read at least four groups before its MFMA: the step's K
+// fragments at its start (the P.V MFMAs come first), the V^T fragments of the
+// next step's P.V during this step's K.Q^T.  Block j's sums are checked at
+// the end of step j, before its P.V in step j + 1.  A 64-key tile (two
+// blocks) is read for its K from the step before its first block's softmax
+// and for its V^T until the step of its last one: two tiles are in use, one
+// is landing and a fourth buffer is being filled.  Tiles go straight from
+// memory into four LDS buffers (global_load_lds), issued three tiles ahead,
+// with one barrier per tile.
 template <int P>
 __global__ __launch_bounds__(256, 2) void k_attn_bf(AttnArgs a) {
   using M = Mfma<bf16>;
@@ -1053,7 +1077,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf(AttnArgs a) {
       for (int kb = 0; kb < 2; ++kb) r |= key_masked<P>(x.ln, kb * 32 + l32) ? 1 << kb : 0;
       return r;
     };
-    auto ready = [](typename DL::Ids& x) __attribute__((always_inline)) { asm volatile("" : "+v"(x.pg), "+v"(x.ln)); };
+    auto ready = [](typename DL::Ids& x) __attribute__((always_inline)) { asm volatile("" : "+s"(x.pg), "+s"(x.ln)); };
 
     // raw scores of key block kb of the tile in buffer b (mask bits mi)
     auto qk_raw = [&](const char* b, int kb, int mi, floatx16 (&s)[NQB]) __attribute__((always_inline)) {
@@ -1081,32 +1105,34 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf(AttnArgs a) {
         }
       }
     };
-    // One step: K.Q^T of block qkb of buffer qbuf into sQ (mask bits qmi),
-    // softmax of sS into pS, P.V of pV with block vkb of buffer vbuf.  Issued
-    // in 17 groups, each an MFMA and six VALU instructions of the softmax (two
-    // elements: their scaled logits and exponentials, one bf16 pack, one
-    // row-sum dot product), kept in this order by scheduling barriers: the
-    // mask product first (no LDS operand), the K.Q^T MFMAs while the V^T
-    // fragments land, then the P.V MFMAs.
-    auto step = [&](const char* qbuf, int qkb, int qmi, const char* vbuf, int vkb, floatx16 (&sQ)[NQB],
-                    floatx16 (&sS)[NQB], Frag (&pS)[NCH][NQB], const Frag (&pV)[NCH][NQB], float (&ts)[NQB])
-        __attribute__((always_inline)) {
+    // One step: P.V of pV with the V^T fragments vfc (read during the
+    // previous step), softmax of sS into pS, K.Q^T of block qkb of buffer
+    // qbuf into sQ (mask bits qmi), and the V^T fragments of the next step's
+    // P.V (block nvkb of buffer nvbuf) into vfn.  Issued in 17 groups, each an
+    // MFMA and six VALU instructions of the softmax (two elements: their
+    // scaled logits and exponentials, one bf16 pack, one row-sum dot
+    // product), kept in this order by scheduling barriers: the eight P.V
+    // MFMAs first, while this step's K fragments land, then the mask product
+    // (no LDS operand), then the K.Q^T MFMAs while the next V^T fragments land.
+    auto step = [&](const char* qbuf, int qkb, int qmi, const Frag (&vfc)[NCH][2], const char* nvbuf, int nvkb,
+                    Frag (&vfn)[NCH][2], floatx16 (&sQ)[NQB], floatx16 (&sS)[NQB], Frag (&pS)[NCH][NQB],
+                    const Frag (&pV)[NCH][NQB], float (&ts)[NQB]) __attribute__((always_inline)) {
       typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
       bf16x2 one;
       one[0] = (bf16)1.0f;
       one[1] = (bf16)1.0f;
-      // K fragments dc = 0, 1 now, 2 and 3 two groups before their MFMAs;
-      // the V^T fragments likewise, spread over groups 3 .. 7
       Frag kf[NDC];
 #pragma unroll
-      for (int dc = 0; dc < 2; ++dc) kf[dc] = read_k((const bf16*)qbuf, 0, qkb * 32 + l32, dc, hi);
+      for (int dc = 0; dc < NDC; ++dc) kf[dc] = read_k((const bf16*)qbuf, 0, qkb * 32 + l32, dc, hi);
       ts[0] = 0.f;
       ts[1] = 0.f;
       // softmax work of group g: the scaled logits and exponentials of
-      // elements 2i, 2i + 1 of query block qb = g / 8 (pair g), and the bf16
-      // pack and row-sum dot product of pair g - 1, whose exponentials were
-      // issued a group earlier (pair 16 closes the step)
+      // elements 2i, 2i + 1 of query block qb = g / 8 (pair g), the bf16 pack
+      // of pair g - 1 (its exponentials issued a group earlier) and the
+      // row-sum dot product of pair g - 2 (packed a group earlier), so that no
+      // instruction waits on the one before it; pairs 15 and 16 close the step
       float xe[2];
+      bf16x2 pk;
       auto valu = [&](int g) __attribute__((always_inline)) {
         float xn[2];
         if (g < 16) {
@@ -1114,7 +1140,11 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf(AttnArgs a) {
           xn[0] = __builtin_fmaf(sS[qb][2 * i], qs, nm[qb]);
           xn[1] = __builtin_fmaf(sS[qb][2 * i + 1], qs, nm[qb]);
         }
-        if (g > 0) {
+        if (g > 1 && g < 18) {
+          const int qb = (g - 2) >> 3;
+          ts[qb] = __builtin_amdgcn_fdot2_f32_bf16(pk, one, ts[qb], false);
+        }
+        if (g > 0 && g < 17) {
           const int gp = g - 1, qb = gp >> 3, i = gp & 7, ch = i >> 2, k = i & 3;
           bf16x2 pr;
           pr[0] = (bf16)xe[0];
@@ -1123,43 +1153,41 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf(AttnArgs a) {
           // end of the step, past the sum check)
           uint32_t u = __builtin_bit_cast(uint32_t, pr);
           asm volatile("" : "+v"(u));
-          pr = __builtin_bit_cast(bf16x2, u);
-          pS[ch][qb][2 * k] = pr[0];
-          pS[ch][qb][2 * k + 1] = pr[1];
-          ts[qb] = __builtin_amdgcn_fdot2_f32_bf16(pr, one, ts[qb], false);
+          pk = __builtin_bit_cast(bf16x2, u);
+          pS[ch][qb][2 * k] = pk[0];
+          pS[ch][qb][2 * k + 1] = pk[1];
         }
         if (g < 16) {
           xe[0] = __builtin_amdgcn_exp2f(xn[0]);
           xe[1] = __builtin_amdgcn_exp2f(xn[1]);
         }
       };
-      // group 0: the mask product (all zero in a full tile)
+      // groups 0 .. 7: P.V
+#pragma unroll
+      for (int g = 0; g < 8; ++g) {
+        const int c = g >> 2, db = (g >> 1) & 1, qb = g & 1;
+        o[db][qb] = M::mma(vfc[c][db], pV[c][qb], o[db][qb]);
+        valu(g);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // group 8: the mask product (all zero in a full tile)
       const floatx16 s0 = M::mma_seed(M::mask_a((qmi >> qkb) & 1, hi), M::mask_b(hi));
-      valu(0);
+      valu(8);
       __builtin_amdgcn_sched_barrier(0);
-      Frag vf[NCH][2];
-      // groups 1 .. 8: K.Q^T (the V^T fragments read after the first two)
+      // groups 9 .. 16: K.Q^T, the next V^T fragments read in the first four
 #pragma unroll
       for (int g = 0; g < 8; ++g) {
         const int dc = g >> 1, qb = g & 1;
         sQ[qb] = M::mma(kf[dc], qf[qb][dc], dc == 0 ? s0 : sQ[qb]);
-        if (g < 7) valu(g + 1);
-        if (g == 0 || g == 2) kf[2 + g / 2] = read_k((const bf16*)qbuf, 0, qkb * 32 + l32, 2 + g / 2, hi);
-        if (g >= 3 && g < 7) {
-          const int c = (g - 3) >> 1, db = (g - 3) & 1;
-          vf[c][db] = read_v((const bf16*)(vbuf + DL::KBYTES), 0, db * 32 + l32, vkb, c, hi);
+        if (g < 7) valu(g + 9);
+        if (g < 4) {
+          const int c = g >> 1, db = g & 1;
+          vfn[c][db] = read_v((const bf16*)(nvbuf + DL::KBYTES), 0, db * 32 + l32, nvkb, c, hi);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
-      // groups 9 .. 16: P.V
-#pragma unroll
-      for (int g = 0; g < 8; ++g) {
-        const int c = g >> 2, db = (g >> 1) & 1, qb = g & 1;
-        o[db][qb] = M::mma(vf[c][db], pV[c][qb], o[db][qb]);
-        valu(g + 8);
-        __builtin_amdgcn_sched_barrier(0);
-      }
       valu(16);
+      valu(17);
     };
     // the sum check of block kb of buffer b after its softmax: if some lane's
     // sum exceeds 2^16, the block's raw scores again (its tile is still in
@@ -1195,10 +1223,10 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf(AttnArgs a) {
 
     // Prologue: page ids and lengths of tiles t0 .. t0 + 3, then the data of
     // t0 .. t0 + 2.  From then on every tile period issues the ids of tile
-    // t + 4 and then tile t + 3's data (four loads) after its barrier, so
-    // waiting for all but the last four vector-memory operations before the
-    // next barrier leaves only the newest tile's data in flight: the tile
-    // needed next has landed and the ids to issue have arrived.
+    // t + 4 (scalar loads, used a period later) and then tile t + 3's data
+    // (four vector-memory loads) after its barrier, so waiting for all but
+    // the last four vector-memory operations before the next barrier leaves
+    // only the newest tile's data in flight: the tile needed next has landed.
     typename DL::Ids ida, idb, idc, idd;
     ld.fetch(a, t0, ida);
     ld.fetch(a, t0 + 1, idb);
@@ -1228,19 +1256,25 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf(AttnArgs a) {
 
     floatx16 s0[NQB], s1[NQB];
     Frag p0[NCH][NQB], p1[NCH][NQB];
+    Frag va[NCH][2], vb[NCH][2];  // V^T fragments of the next P.V, read a step ahead
 #pragma unroll
     for (int ch = 0; ch < NCH; ++ch)
 #pragma unroll
       for (int qb = 0; qb < NQB; ++qb) p1[ch][qb] = Frag{};  // the P.V of step 0 adds nothing
     float ts[NQB];
     qk_raw(buf(0), 0, mr & 3, s0);
+#pragma unroll
+    for (int c = 0; c < NCH; ++c)
+#pragma unroll
+      for (int db = 0; db < 2; ++db) va[c][db] = read_v((const bf16*)(buf(0) + DL::KBYTES), 0, db * 32 + l32, 1, c, hi);
 
     // one tile period; `use` holds the ids of tile t + 3, `next` receives those of t + 4
     auto period = [&](int i, typename DL::Ids& use, typename DL::Ids& next) __attribute__((always_inline)) {
       const int t = t0 + i;
-      // step 2i: QK of block 1 of tile t, softmax of block 0 of tile t, P.V of
-      // block 1 of tile t - 1 (of tile t with P = 0 in the first step)
-      step(buf(i), 1, mr & 3, buf(i > 0 ? i - 1 : i), 1, s1, s0, p0, p1, ts);
+      // step 2i: P.V of block 1 of tile t - 1 (of tile t with P = 0 in the
+      // first step), softmax of block 0 of tile t, QK of block 1 of tile t;
+      // reads the V^T of block 0 of tile t for the next step
+      step(buf(i), 1, mr & 3, va, buf(i), 0, vb, s1, s0, p0, p1, ts);
       settle(buf(i), 0, mr & 3, s0, p0, ts);
       // tile t + 1 has landed; tile t - 1's buffer is free: ids of tile t + 4,
       // data of tile t + 3 (past the split's end they are read and unused)
@@ -1254,9 +1288,9 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf(AttnArgs a) {
       ld.issue(kp, vp, use, buf(i + 3), wave);
       mr |= minfo(use) << 6;
       asm volatile("" ::: "memory");
-      // step 2i + 1: QK of block 0 of tile t + 1, softmax of block 1 of tile t,
-      // P.V of block 0 of tile t
-      step(buf(i + 1), 0, (mr >> 2) & 3, buf(i), 0, s0, s1, p1, p0, ts);
+      // step 2i + 1: P.V of block 0 of tile t, softmax of block 1 of tile t,
+      // QK of block 0 of tile t + 1; reads the V^T of block 1 of tile t
+      step(buf(i + 1), 0, (mr >> 2) & 3, vb, buf(i), 1, va, s0, s1, p1, p0, ts);
       settle(buf(i), 1, mr & 3, s1, p1, ts);
       mr >>= 2;
     };
@@ -1267,18 +1301,13 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf(AttnArgs a) {
       if (i + 2 < n) period(i + 2, idb, ida);
       if (i + 3 < n) period(i + 3, ida, idb);
     }
-    // the last block's P.V
-    {
-      const char* vb = buf(n - 1);
+    // the last block's P.V (its V^T fragments read by the last step)
 #pragma unroll
-      for (int ch = 0; ch < NCH; ++ch)
+    for (int ch = 0; ch < NCH; ++ch)
 #pragma unroll
-        for (int db = 0; db < 2; ++db) {
-          const Frag vf = read_v((const bf16*)(vb + DL::KBYTES), 0, db * 32 + l32, 1, ch, hi);
+      for (int db = 0; db < 2; ++db)
 #pragma unroll
-          for (int qb = 0; qb < NQB; ++qb) o[db][qb] = M::mma(vf, p1[ch][qb], o[db][qb]);
-        }
-    }
+        for (int qb = 0; qb < NQB; ++qb) o[db][qb] = M::mma(va[ch][db], p1[ch][qb], o[db][qb]);
     // the loads issued past the last tile land before the workgroup's LDS is reused
     wait_vmem<0>();
   }
