@@ -78,14 +78,17 @@ def kernel_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def counters_from_profiles(kh: str) -> dict:
-    """The committed counter summary of the attention kernel, if it is of this source."""
+def counters_from_profiles(kh: str, workload: str) -> dict:
+    """The committed counter summary of the attention kernel on `workload`, if
+    it was taken from this kernel source."""
     p = os.path.join(ROOT, "profiles", "attn_traffic.json")
     try:
         d = json.load(open(p))
     except (OSError, ValueError):
         return {}
-    return d if d.get("kernel_hash") == kh else {}
+    if d.get("kernel_hash") != kh:
+        return {}
+    return d.get("workloads", {}).get(workload, {})
 
 
 def stage_frames(w, fs, dt, n_stage):
@@ -455,22 +458,29 @@ def run_cpu_baseline(w, n_ctx):
         t_book += time.perf_counter() - a
         if f in (fa, fb):
             q = fs.q(f)
-            a = time.perf_counter()
-            c.attend(f, q, threads=threads)
-            timed[f] = (time.perf_counter() - a, c.n_ctx())
+            # repeated until at least 50 ms have passed, so that small frames time reliably
+            reps, a = 0, time.perf_counter()
+            while True:
+                c.attend(f, q, threads=threads)
+                reps += 1
+                el = time.perf_counter() - a
+                if el >= 0.05:
+                    break
+            timed[f] = (el / reps, c.n_ctx())
         if not key:
             a = time.perf_counter()
             c.rollback(f)
             t_book += time.perf_counter() - a
     book = t_book / (fb + 1)
     (ta, na), (tb, nb) = timed[fa], timed[fb]
-    slope = (tb - ta) / (nb - na) if nb != na else tb / nb
+    # a + b*n_ctx through the two frames, neither part negative
+    slope = max(0.0, (tb - ta) / (nb - na)) if nb != na else tb / nb
     icpt = max(0.0, tb - slope * nb)
     est = w.n_frames * book + sum(icpt + slope * n for n in n_ctx)
     return dict(value=w.n_frames / est, unit="frames/s/layer", cores=threads, kind="oracle",
                 cpu_model=_cpu_model(),
-                full_row_frames={str(fa): {"n_ctx": na, "s": round(ta, 3)},
-                                 str(fb): {"n_ctx": nb, "s": round(tb, 3)}},
+                full_row_frames={str(fa): {"n_ctx": na, "s": round(ta, 6)},
+                                 str(fb): {"n_ctx": nb, "s": round(tb, 6)}},
                 bookkeeping_s_per_frame=round(book, 5),
                 sample=(f"{w.name}: bookkeeping (append/evict/rollback with data) of frames 0..{fb}, "
                         f"attention for all {w.T} query rows x {w.H} heads at frames {fa} and {fb} "
@@ -501,7 +511,8 @@ def stream_line(w, steps, warmup, cpu: bool):
                    **({"infer_window": w.infer_window, "infer_overlap": w.infer_overlap}
                       if w.infer_window else {})},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
-                     "frac": round(achieved / peak, 4)},
+                     "frac": round(achieved / peak, 4),
+                     "traffic": counters_from_profiles(kernel_hash(), w.name).get("bytes_per_launch")},
         "steady_state": {"frames": list(r["tail_frames"]), "value": round(r["tail_fps"], 2),
                          "unit": "frames/s/layer"},
         "append_compact": append_compact_line(w, r["kern"]),
@@ -528,9 +539,7 @@ def main():
     cpu = not args.no_cpu_baseline
     head, r = stream_line(w, args.steps, args.warmup, cpu=False)
     kh = kernel_hash()
-    ctr = counters_from_profiles(kh)
-    traffic = ctr.get("bytes_per_launch")
-    head["roofline"]["traffic"] = traffic if traffic is None else round(traffic)
+    ctr = counters_from_profiles(kh, w.name)
 
     line = {
         "metric": METRIC,

@@ -208,9 +208,14 @@ def test_committed_counter_summary_fields():
     import json
     root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
     d = json.load(open(os.path.join(root, "profiles", "attn_traffic.json")))
-    for key in ("kernel_hash", "mfma_busy", "bytes_per_launch", "fetch_scale", "write_scale"):
+    for key in ("kernel_hash", "fetch_scale", "write_scale", "workloads"):
         assert key in d
-    assert 0 < d["mfma_busy"] < 1 and d["bytes_per_launch"] > 0 and len(d["kernel_hash"]) == 16
+    assert len(d["kernel_hash"]) == 16
+    from paged_kv_cache_gca_amd import workloads as WL
+    assert WL.FRAME1004_W16.name in d["workloads"]
+    for name, e in d["workloads"].items():
+        assert name in {w.name for w in WL.ALL}
+        assert 0 < e["mfma_busy"] < 1 and e["bytes_per_launch"] > 0
 
 
 def test_binding_refuses_bad_tensors_before_the_library():
