@@ -498,6 +498,15 @@ def stream_line(w, steps, warmup, cpu: bool):
     avg_attn_s = attn_ms / 1e3 / max(attn_n, 1)
     achieved = flop_per_launch / avg_attn_s / 1e12
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_MFMA_TFLOPS
+    # the attention together with its split merge: the merge's kernel duration from the committed
+    # kernel trace of this kernel source (HIP events around a 7 us launch add several us), else null
+    merge_us = counters_from_profiles(kernel_hash(), w.name).get("merge_us_per_frame")
+    with_merge = None
+    if merge_us is not None:
+        t = avg_attn_s + merge_us * 1e-6
+        with_merge = {"merge_us_per_frame": merge_us, "merge_source": "rocprofv3 kernel trace",
+                      "achieved": round(flop_per_launch / t / 1e12, 2),
+                      "frac": round(flop_per_launch / t / 1e12 / peak, 4), "unit": "TFLOP/s"}
     line = {
         "workload": w.name,
         "value": round(steps * w.n_frames / r["seconds"], 2),
@@ -513,6 +522,7 @@ def stream_line(w, steps, warmup, cpu: bool):
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(achieved / peak, 4),
                      "traffic": counters_from_profiles(kernel_hash(), w.name).get("bytes_per_launch")},
+        "with_merge": with_merge,
         "steady_state": {"frames": list(r["tail_frames"]), "value": round(r["tail_fps"], 2),
                          "unit": "frames/s/layer"},
         "append_compact": append_compact_line(w, r["kern"]),
@@ -557,6 +567,7 @@ def main():
         "config": {"workload": w.name, **{k: v for k, v in head["config"].items() if k != "drift_sigma"},
                    "rope": "3d" if w.rope else "none", "parallelism": "none (1 GPU)"},
         "roofline": head["roofline"],
+        "attn_with_merge": head["with_merge"],
         "steady_state": head["steady_state"],
         "mfma_busy": ctr.get("mfma_busy"),
         "append_compact": head["append_compact"],
