@@ -178,3 +178,25 @@ def test_windowed_append_frames_and_errors():
     x = torch.zeros((w.T, w.H, w.D), dtype=torch.bfloat16, device="cuda")
     assert p.gpu.rope3d(w.infer_window - 1, x, torch.empty_like(x)) == 0
     assert p.gpu.rope3d(w.infer_window, x, torch.empty_like(x)) == g.GCA_ERR_CAPACITY
+
+
+def test_windowed_step_static_matches_step_bitwise():
+    """gca_step_static (scratch in the library's static array) starts the
+    windows exactly as gca_step does: the same outputs bit for bit."""
+    g = gca()
+    w = WL.WINDOWED_SMALL_F32
+    a = g.Cache(g.Config.from_workload(w))
+    b = g.Cache(g.Config.from_workload(w))
+    p = Pair(w)
+    for f in range(w.n_frames):
+        key = w.is_keyframe(f)
+        _, _, kd, vd = p.kv(f)
+        qd = dev(p.fs.q(f), w.dtype)
+        oa = torch.empty((w.T, w.H, w.D), dtype=torch.float32, device="cuda")
+        ob = torch.empty_like(oa)
+        la = torch.empty((w.T, w.H), dtype=torch.float32, device="cuda")
+        lb = torch.empty_like(la)
+        assert a.step(f, kd, vd, qd, oa, la, keyframe=key) == 0
+        assert b.step_static(f, kd, vd, qd, ob, lb, keyframe=key) == 0
+        assert torch.equal(oa, ob) and torch.equal(la, lb), f
+    assert a.query().window_origin == b.query().window_origin > 0
