@@ -467,10 +467,10 @@ int gca_cache_create(const gca_config* cfg, gca_cache** out) {
       cus > 0)
     c->num_cu = cus;
   c->esize = g.dtype == GCA_BF16 ? 2 : 4;
-  // measured optimum: the second-dispatched split's tiles cost 1.56x the
-  // first's at P = 16 (register-staged tiles) and 1.84x at P = 64 (tiles
-  // loaded straight into LDS), and the first one speeds up once it runs alone
-  c->split_ratio = g.P >= 64 ? 1.9f : 1.7f;
+  // the first-dispatched workgroup of a CU issues ahead of the second, and
+  // speeds up once it runs alone; sweeps of the ratio from 1.4 to 2.5 were
+  // best from 2.2 on, within 1.5 % over the whole range
+  c->split_ratio = g.P >= 64 ? 2.3f : 2.2f;
   size_t page_elems = (size_t)g.H * g.P * g.D;
   // pages [0, N) are handed out by the ring; page N stays zero forever and
   // pads the gather list
