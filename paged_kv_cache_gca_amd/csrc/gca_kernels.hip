@@ -1040,6 +1040,9 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf(AttnArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hi = lane >> 5;
   const int qbase = (qt * kWaves + wave) * 64;
+  // bf16 1.0 in the lanes that hold column 0 of a seed A operand, else 0: a
+  // seed operand is the key's mask bit times this (M::mask_a in two instructions)
+  const int one_hi = hi == 0 ? M::bits(1.f) : 0;
 
   Frag qf[NQB][NDC];
   load_q(a, qbase, h, l32, hi, qf);
@@ -1084,7 +1087,8 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf(AttnArgs a) {
       Frag kf[NDC];
 #pragma unroll
       for (int dc = 0; dc < NDC; ++dc) kf[dc] = read_k((const bf16*)b, 0, kb * 32 + l32, dc, hi);
-      const floatx16 s0 = M::mma_seed(M::mask_a((mi >> kb) & 1, hi), M::mask_b(hi));
+      u32x2 sw = {(uint32_t)(-((mi >> kb) & 1) & one_hi), 0u};
+      const floatx16 s0 = M::mma_seed(__builtin_bit_cast(typename M::Seed, sw), M::mask_b(hi));
 #pragma unroll
       for (int qb = 0; qb < NQB; ++qb) {
         s[qb] = M::mma(kf[0], qf[qb][0], s0);
@@ -1124,8 +1128,6 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf(AttnArgs a) {
       Frag kf[NDC];
 #pragma unroll
       for (int dc = 0; dc < NDC; ++dc) kf[dc] = read_k((const bf16*)qbuf, 0, qkb * 32 + l32, dc, hi);
-      ts[0] = 0.f;
-      ts[1] = 0.f;
       // softmax work of group g: the scaled logits and exponentials of
       // elements 2i, 2i + 1 of query block qb = g / 8 (pair g), the bf16 pack
       // of pair g - 1 (its exponentials issued a group earlier) and the
@@ -1141,8 +1143,9 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf(AttnArgs a) {
           xn[1] = __builtin_fmaf(sS[qb][2 * i + 1], qs, nm[qb]);
         }
         if (g > 1 && g < 18) {
+          // the first pair of each query block starts its sum
           const int qb = (g - 2) >> 3;
-          ts[qb] = __builtin_amdgcn_fdot2_f32_bf16(pk, one, ts[qb], false);
+          ts[qb] = __builtin_amdgcn_fdot2_f32_bf16(pk, one, ((g - 2) & 7) == 0 ? 0.f : ts[qb], false);
         }
         if (g > 0 && g < 17) {
           const int gp = g - 1, qb = gp >> 3, i = gp & 7, ch = i >> 2, k = i & 3;
@@ -1171,7 +1174,8 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf(AttnArgs a) {
         __builtin_amdgcn_sched_barrier(0);
       }
       // group 8: the mask product (all zero in a full tile)
-      const floatx16 s0 = M::mma_seed(M::mask_a((qmi >> qkb) & 1, hi), M::mask_b(hi));
+      u32x2 sw = {(uint32_t)(-((qmi >> qkb) & 1) & one_hi), 0u};
+      const floatx16 s0 = M::mma_seed(__builtin_bit_cast(typename M::Seed, sw), M::mask_b(hi));
       valu(8);
       __builtin_amdgcn_sched_barrier(0);
       // groups 9 .. 16: K.Q^T, the next V^T fragments read in the first four
