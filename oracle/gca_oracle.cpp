@@ -37,6 +37,9 @@
 //    the last `overlap` keyframes that fit in a window with the new frame are
 //    appended again from their raw K/V (oldest first, at positions relative
 //    to the new origin, which is the oldest of them), then the frame itself.
+//    The pages give no restart rule: parity unpinned by the pages (pinned to
+//    this reading by hand-derived sizes, positions and live frames in the
+//    tests, and by a restarted window equalling a fresh cache).
 //
 // Readings where the pages are silent (each is a choice, mirrored by the HIP
 // library's own independent code):
