@@ -203,6 +203,16 @@ def test_bench_refuses_more_than_one_gpu():
     assert "one GPU" in json.loads(r.stdout.strip().splitlines()[-1])["error"]
 
 
+def test_bench_cpu_baseline_model_is_positive():
+    """The CPU baseline's per-frame model (bookkeeping plus a + b*n_ctx through
+    two timed frames) stays positive on tiny frames, where timing noise can
+    make the later frame time shorter than the earlier one."""
+    import bench
+    for w in (WL.TINY_F32, WL.CAMERA_T1):
+        r = bench.run_cpu_baseline(w, bench.plan_n_ctx(w))
+        assert r["value"] > 0 and r["kind"] == "oracle" and r["cores"] >= 1
+
+
 def test_committed_counter_summary_fields():
     """profiles/attn_traffic.json carries what the bench line reads from it."""
     import json
