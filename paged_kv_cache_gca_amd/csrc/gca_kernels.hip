@@ -713,21 +713,24 @@ struct DmaLoader {
   }
 };
 
-// Row sums of P from the same rounded values the P.V product uses (this
-// lane's keys only; the lane pair l, l ^ 32 covers the whole tile).
-__device__ inline float rowsum_add(float l, bf16x8 p) {
-  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-  bf16x2 one;
-  one[0] = (bf16)1.0f;
-  one[1] = (bf16)1.0f;
+// Row sums of P on the matrix cores, from the same rounded values the P.V
+// product uses.  A P^T operand (16 keys x 32 queries) gives lane (l32, hi)
+// eight keys of query l32.  In a 16x16x32 product lane l supplies row l % 16
+// (A) or column l % 16 (B) of lane group l / 16, and holds rows
+// 4 * (l / 16) .. + 3 of column l % 16 of the result.  With A row m set to
+// one over lane groups g where g % 2 == (m / 4) % 2, column n of result row m
+// sums the keys of query n + 16 * ((m / 4) % 2) held by both halves of the
+// wave, so every lane's result (all four registers alike) is the sum over
+// the operand's 16 keys of its own query l32.
+__device__ inline bf16x8 rowsum_selector(int lane) {
+  const bf16 v = (bf16)((((lane & 15) >> 2) & 1) == ((lane >> 4) & 1) ? 1.f : 0.f);
+  bf16x8 r;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    bf16x2 pr;
-    pr[0] = p[2 * i];
-    pr[1] = p[2 * i + 1];
-    l = __builtin_amdgcn_fdot2_f32_bf16(pr, one, l, false);
-  }
-  return l;
+  for (int i = 0; i < 8; ++i) r[i] = v;
+  return r;
+}
+__device__ inline floatx4 rowsum_mma(bf16x8 sel, bf16x8 p, floatx4 acc) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(sel, p, acc, 0, 0, 0);
 }
 
 // s_waitcnt on the vector-memory count only (vmcnt <= N, N < 16): bits 3:0
@@ -1014,9 +1017,10 @@ __device__ inline void attn_epilogue_bf(const AttnArgs& a, const floatx16 (&o)[2
 //
 // Workgroup shape, mapping and splits as in k_attn.  Step j of a wave issues,
 // independently of one another, the P.V MFMAs of key block j - 1, the
-// softmax of block j (scaling, exponentials, packing, row sums: VALU) and the
-// K.Q^T MFMAs of block j + 1, interleaved one MFMA to six VALU instructions,
-// so that the matrix and vector pipes of a SIMD stay busy together.  Every LDS
+// softmax of block j (scaling, exponentials and packing on the VALU, the row
+// sums on the matrix cores) and the K.Q^T MFMAs of block j + 1, interleaved
+// one MFMA to five VALU instructions, so that the matrix and vector pipes of
+// a SIMD stay busy together.  Every LDS
 // operand is read at least four groups before its MFMA: the step's K
 // fragments at its start (the P.V MFMAs come first), the V^T fragments of the
 // next step's P.V during this step's K.Q^T.  Block j's sums are checked at
@@ -1043,6 +1047,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf(AttnArgs a) {
   // bf16 1.0 in the lanes that hold column 0 of a seed A operand, else 0: a
   // seed operand is the key's mask bit times this (M::mask_a in two instructions)
   const int one_hi = hi == 0 ? M::bits(1.f) : 0;
+  const Frag sel = rowsum_selector(lane);
 
   Frag qf[NQB][NDC];
   load_q(a, qbase, h, l32, hi, qf);
@@ -1096,43 +1101,38 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf(AttnArgs a) {
         for (int dc = 1; dc < NDC; ++dc) s[qb] = M::mma(kf[dc], qf[qb][dc], s[qb]);
       }
     };
-    auto softmax = [&](floatx16 (&s)[NQB], Frag (&p)[NCH][NQB], float (&ts)[NQB]) __attribute__((always_inline)) {
+    auto softmax = [&](floatx16 (&s)[NQB], Frag (&p)[NCH][NQB], floatx4 (&ts)[NQB]) __attribute__((always_inline)) {
 #pragma unroll
       for (int qb = 0; qb < NQB; ++qb) {
-        ts[qb] = 0.f;
 #pragma unroll
         for (int r = 0; r < 16; ++r) s[qb][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][r], qs, nm[qb]));
 #pragma unroll
-        for (int ch = 0; ch < NCH; ++ch) {
-          p[ch][qb] = pack_p(s[qb], ch, bf16());
-          ts[qb] = rowsum_add(ts[qb], p[ch][qb]);
-        }
+        for (int ch = 0; ch < NCH; ++ch) p[ch][qb] = pack_p(s[qb], ch, bf16());
+        ts[qb] = rowsum_mma(sel, p[1][qb], rowsum_mma(sel, p[0][qb], floatx4{0.f, 0.f, 0.f, 0.f}));
       }
     };
     // One step: P.V of pV with the V^T fragments vfc (read during the
     // previous step), softmax of sS into pS, K.Q^T of block qkb of buffer
     // qbuf into sQ (mask bits qmi), and the V^T fragments of the next step's
     // P.V (block nvkb of buffer nvbuf) into vfn.  Issued in 17 groups, each an
-    // MFMA and six VALU instructions of the softmax (two elements: their
-    // scaled logits and exponentials, one bf16 pack, one row-sum dot
-    // product), kept in this order by scheduling barriers: the eight P.V
-    // MFMAs first, while this step's K fragments land, then the mask product
-    // (no LDS operand), then the K.Q^T MFMAs while the next V^T fragments land.
+    // MFMA and five VALU instructions of the softmax (two elements: their
+    // scaled logits and exponentials, one bf16 pack), kept in this order by
+    // scheduling barriers: the eight P.V MFMAs first, while this step's K
+    // fragments land, then the mask product (no LDS operand), then the K.Q^T
+    // MFMAs while the next V^T fragments land.  The row sums of the new P go
+    // to the matrix cores as well, one 16x16x32 product per packed operand, a
+    // group after its last pack.
     auto step = [&](const char* qbuf, int qkb, int qmi, const Frag (&vfc)[NCH][2], const char* nvbuf, int nvkb,
                     Frag (&vfn)[NCH][2], floatx16 (&sQ)[NQB], floatx16 (&sS)[NQB], Frag (&pS)[NCH][NQB],
-                    const Frag (&pV)[NCH][NQB], float (&ts)[NQB]) __attribute__((always_inline)) {
+                    const Frag (&pV)[NCH][NQB], floatx4 (&ts)[NQB]) __attribute__((always_inline)) {
       typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-      bf16x2 one;
-      one[0] = (bf16)1.0f;
-      one[1] = (bf16)1.0f;
       Frag kf[NDC];
 #pragma unroll
       for (int dc = 0; dc < NDC; ++dc) kf[dc] = read_k((const bf16*)qbuf, 0, qkb * 32 + l32, dc, hi);
       // softmax work of group g: the scaled logits and exponentials of
-      // elements 2i, 2i + 1 of query block qb = g / 8 (pair g), the bf16 pack
-      // of pair g - 1 (its exponentials issued a group earlier) and the
-      // row-sum dot product of pair g - 2 (packed a group earlier), so that no
-      // instruction waits on the one before it; pairs 15 and 16 close the step
+      // elements 2i, 2i + 1 of query block qb = g / 8 (pair g) and the bf16
+      // pack of pair g - 1 (its exponentials issued a group earlier), so that
+      // no instruction waits on the one before it; pair 15's pack closes the step
       float xe[2];
       bf16x2 pk;
       auto valu = [&](int g) __attribute__((always_inline)) {
@@ -1141,11 +1141,6 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf(AttnArgs a) {
           const int qb = g >> 3, i = g & 7;
           xn[0] = __builtin_fmaf(sS[qb][2 * i], qs, nm[qb]);
           xn[1] = __builtin_fmaf(sS[qb][2 * i + 1], qs, nm[qb]);
-        }
-        if (g > 1 && g < 18) {
-          // the first pair of each query block starts its sum
-          const int qb = (g - 2) >> 3;
-          ts[qb] = __builtin_amdgcn_fdot2_f32_bf16(pk, one, ((g - 2) & 7) == 0 ? 0.f : ts[qb], false);
         }
         if (g > 0 && g < 17) {
           const int gp = g - 1, qb = gp >> 3, i = gp & 7, ch = i >> 2, k = i & 3;
@@ -1170,6 +1165,8 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf(AttnArgs a) {
       for (int g = 0; g < 8; ++g) {
         const int c = g >> 2, db = (g >> 1) & 1, qb = g & 1;
         o[db][qb] = M::mma(vfc[c][db], pV[c][qb], o[db][qb]);
+        // pairs 0-3 (query block 0, keys of chunk 0) were packed in group 4
+        if (g == 5) ts[0] = rowsum_mma(sel, pS[0][0], floatx4{0.f, 0.f, 0.f, 0.f});
         valu(g);
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -1183,6 +1180,8 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf(AttnArgs a) {
       for (int g = 0; g < 8; ++g) {
         const int dc = g >> 1, qb = g & 1;
         sQ[qb] = M::mma(kf[dc], qf[qb][dc], dc == 0 ? s0 : sQ[qb]);
+        if (g == 0) ts[0] = rowsum_mma(sel, pS[1][0], ts[0]);
+        if (g == 4) ts[1] = rowsum_mma(sel, pS[0][1], floatx4{0.f, 0.f, 0.f, 0.f});
         if (g < 7) valu(g + 9);
         if (g < 4) {
           const int c = g >> 1, db = g & 1;
@@ -1191,17 +1190,18 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf(AttnArgs a) {
         __builtin_amdgcn_sched_barrier(0);
       }
       valu(16);
-      valu(17);
+      __builtin_amdgcn_sched_barrier(0);
+      ts[1] = rowsum_mma(sel, pS[1][1], ts[1]);
     };
-    // the sum check of block kb of buffer b after its softmax: if some lane's
-    // sum exceeds 2^16, the block's raw scores again (its tile is still in
+    // the sum check of block kb of buffer b after its softmax: if the sum of
+    // some query's P over the block exceeds 2^16, the block's raw scores again (its tile is still in
     // LDS), m raised to the block max where that exceeds it by more than
     // kRaise (O and l rescaled), then the softmax again
-    auto settle = [&](const char* b, int kb, int mi, floatx16 (&s)[NQB], Frag (&p)[NCH][NQB], float (&ts)[NQB])
+    auto settle = [&](const char* b, int kb, int mi, floatx16 (&s)[NQB], Frag (&p)[NCH][NQB], floatx4 (&ts)[NQB])
         __attribute__((always_inline)) {
       bool bad = false;
 #pragma unroll
-      for (int qb = 0; qb < NQB; ++qb) bad = bad || !(ts[qb] <= kMaxBlockSum);
+      for (int qb = 0; qb < NQB; ++qb) bad = bad || !(ts[qb][0] <= kMaxBlockSum);
       if (__any(bad)) {
         qk_raw(b, kb, mi, s);
 #pragma unroll
@@ -1222,7 +1222,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf(AttnArgs a) {
         softmax(s, p, ts);
       }
 #pragma unroll
-      for (int qb = 0; qb < NQB; ++qb) l[qb] += ts[qb];
+      for (int qb = 0; qb < NQB; ++qb) l[qb] += ts[qb][0];
     };
 
     // Prologue: page ids and lengths of tiles t0 .. t0 + 3, then the data of
@@ -1265,7 +1265,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf(AttnArgs a) {
     for (int ch = 0; ch < NCH; ++ch)
 #pragma unroll
       for (int qb = 0; qb < NQB; ++qb) p1[ch][qb] = Frag{};  // the P.V of step 0 adds nothing
-    float ts[NQB];
+    floatx4 ts[NQB];
     qk_raw(buf(0), 0, mr & 3, s0);
 #pragma unroll
     for (int c = 0; c < NCH; ++c)
@@ -1316,9 +1316,6 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf(AttnArgs a) {
     wait_vmem<0>();
   }
 
-  // each lane summed P over its own half of the keys
-#pragma unroll
-  for (int qb = 0; qb < NQB; ++qb) l[qb] += __shfl_xor(l[qb], 32);
   attn_epilogue_bf(a, o, m, l, split, qbase, h, l32, hi, lane, wave, lt);
 }
 
