@@ -435,24 +435,58 @@ struct Mfma<float> {
 // positions, each row of a pair its own half of the banks.
 __device__ inline int swz(int row, int c) { return row * 128 + ((c ^ ((row >> 1) & 7)) << 4); }
 
-// K operand: key row `row`, dims [dc*2*KPL + hi*KPL, +KPL).
-__device__ inline bf16x8 read_k(const bf16* lk, int pitch, int row, int dc, int hi) {
-  (void)pitch;
-  return *(const bf16x8*)((const char*)lk + swz(row, dc * 2 + hi));
-}
+// fp32 K operand: key row `row`, dim 2 dc + hi.
 __device__ inline float read_k(const float* lk, int pitch, int row, int dc, int hi) {
   return lk[row * pitch + dc * 2 + hi];
 }
 
-// V^T operand for dim row d and chunk ch of key block kb: the keys whose S^T
-// accumulator registers form the matching P^T operand, i.e. keys
-// 16*ch + 4*hi + {0..3} and 16*ch + 8 + 4*hi + {0..3} of the block.  The bf16
-// V^T tile holds each 16-key group in that order (keys 0-3, 8-11, 4-7,
-// 12-15), so the operand is one 16-byte read, laid out like the K reads.
-__device__ inline bf16x8 read_v(const bf16* lv, int pitch, int d, int kb, int ch, int hi) {
-  (void)pitch;
-  return *(const bf16x8*)((const char*)lv + swz(d, kb * 4 + ch * 2 + hi));
-}
+// bf16 V^T tile in LDS: the 16-byte chunk q of dim row d holds key slots
+// 8q .. 8q + 7 of the tile.  The tile is stored page by page, as the pool
+// holds it: page q / (P / 8) of the tile is one block of 64 dim rows of P / 8
+// chunks (128 P bytes), so that one DMA load instruction (1 KB) fills part of
+// one page only.  Inside a block the chunk u of row d sits at position
+// u ^ ((d / R) mod (P / 8)), R = 16 / (P / 8) rows per 256 bytes: the 16
+// rows that one operand read serves together then cover all 64 banks.  At
+// P = 64 this is the K tile's swizzle.
+//
+// Operand reads of the bf16 tiles, from lane offsets computed once.
+// K: key row 32 kb + l32, dims [16 dc + 8 hi, +8) (swz; the row's XOR term
+// does not depend on kb).  V^T: dim row 32 db + l32, chunk 4 kb + 2 ch + hi,
+// i.e. the keys whose S^T accumulator registers form the matching P^T
+// operand, keys 16*ch + 4*hi + {0..3} and 16*ch + 8 + 4*hi + {0..3} of the
+// block; the V^T tile holds each 16-key group in that order (keys 0-3, 8-11,
+// 4-7, 12-15), so the operand is one 16-byte read.  In the V^T layout the
+// row's XOR term does not depend on db, and the chunk splits into a page and
+// an in-page chunk without carries, so only the in-page chunk's XOR takes a
+// lane offset of its own: one at P = 16, two at P = 32, four at P = 64.  The
+// offsets are kept opaque, so that each read is one register plus an
+// immediate.
+template <int P>
+struct TileAddr {
+  static constexpr int CPP = P / 8, R = 16 / CPP, NV = CPP / 2;
+  int k[4], v[NV];
+  __device__ void init(int l32, int hi) {
+#pragma unroll
+    for (int dc = 0; dc < 4; ++dc) {
+      k[dc] = swz(l32, dc * 2 + hi);
+      asm volatile("" : "+v"(k[dc]));
+    }
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      v[i] = l32 * (CPP * 16) + (((2 * i + hi) ^ ((l32 / R) % CPP)) << 4);
+      asm volatile("" : "+v"(v[i]));
+    }
+  }
+  __device__ bf16x8 kop(const char* t, int kb, int dc) const {
+    return *(const bf16x8*)(t + kb * 32 * 128 + k[dc]);
+  }
+  __device__ bf16x8 vop(const char* t, int db, int kb, int ch) const {
+    const int q0 = kb * 4 + ch * 2;
+    return *(const bf16x8*)(t + (q0 / CPP) * (128 * P) + db * (32 * CPP * 16) + v[(q0 % CPP) / 2]);
+  }
+};
+
+// fp32 V^T operand
 __device__ inline float read_v(const float* lv, int pitch, int d, int kb, int ch, int hi) {
   return lv[d * pitch + kb * 32 + (ch >> 2) * 8 + hi * 4 + (ch & 3)];
 }
@@ -657,33 +691,35 @@ struct DmaLoader {
   static constexpr int BUF_BYTES = 2 * KBYTES;
   static constexpr int NISSUE = 4;  // DMA loads per wave and tile
   // the EPT page ids and lengths of a tile: wave-uniform, in scalar
-  // registers; each lane picks its pieces' entries when it issues
+  // registers
   struct Ids {
     i32x4 pg, ln;
   };
   uint32_t page_bytes, head_off;
-  int w, lane;
+  int w, pw;
+  uint32_t koff[2], voff[2];
 
+  // Wave w fills tile bytes [2 KB w, 2 KB (w + 1)) of K and of V^T with its two
+  // loads each: key rows 16 w .. 16 w + 15 and their V^T chunks, all in the
+  // tile's page pw = 16 w / P.  koff and voff are this lane's byte offsets
+  // inside that page's (page, head) block, the same for every tile.
   __device__ void init(int h, int H, int tid) {
     w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: the LDS destinations need no waterfall
-    lane = tid & 63;
+    pw = 16 * w / P;
+    const int lane = tid & 63;
     page_bytes = (uint32_t)(H * P * kHeadDim * 2);
     head_off = (uint32_t)(h * P * kHeadDim * 2);
-  }
-  // piece j of this lane in the K tile: its gather entry and its byte offset
-  // inside a (page, head) block (key row r, logical chunk c of the swizzle)
-  __device__ void kpiece(int j, int& ent, uint32_t& off) const {
-    const int pos = (w * 2 + j) * 64 + lane;
-    const int r = pos >> 3, c = (pos & 7) ^ ((r >> 1) & 7);
-    ent = r / P;
-    off = (uint32_t)(((r % P) * kHeadDim + c * 8) * 2);
-  }
-  // piece j in the V^T tile: dim row d, chunk c of 8 stored slots
-  __device__ void vpiece(int j, int& ent, uint32_t& off) const {
-    const int pos = (w * 2 + j) * 64 + lane;
-    const int d = pos >> 3, c = (pos & 7) ^ ((d >> 1) & 7);
-    ent = (8 * c) / P;
-    off = (uint32_t)((d * P + (8 * c) % P) * 2);
+    constexpr int CPP = P / 8, R = 16 / CPP;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int pos = (w * 2 + j) * 64 + lane;  // 16-byte position in the tile
+      // K: key row r, logical chunk c (the swizzle of swz)
+      const int r = pos >> 3, c = (pos & 7) ^ ((r >> 1) & 7);
+      koff[j] = (uint32_t)(((r % P) * kHeadDim + c * 8) * 2);
+      // V^T: dim row d, chunk u of the page block (the inverse of the V^T layout)
+      const int e = pos % (CPP * 64), d = e / CPP, u = (e % CPP) ^ ((d / R) % CPP);
+      voff[j] = (uint32_t)((d * P + u * 8) * 2);
+    }
   }
   // scalar loads through the constant address space (the gather list is
   // not written during the launch): no vector registers, and nothing for the
@@ -692,23 +728,23 @@ struct DmaLoader {
     x.pg = load_uniform<EPT>(a.sel_page + tile * EPT);
     x.ln = load_uniform<EPT>(a.sel_len + tile * EPT);
   }
-  __device__ void issue(const char* kpool, const char* vpool, const Ids& x, char* buf, int /*wave*/) const {
+  // the tile's data: one scalar base per pool, lane offsets from init
+  __device__ void issue(const char* kpool, const char* vpool, const Ids& x, char* buf, int /*wave*/) {
     typedef __attribute__((address_space(3))) void lds_t;
+    const uint64_t off = (uint64_t)(uint32_t)pick(x.pg, pw) * page_bytes + head_off;
+    const char* kb = kpool + off;
+    const char* vb = vpool + off;
+    // (the 32-bit offsets are pinned here so that each load takes the scalar
+    // base and the offset as they are, not a 64-bit sum made in vector registers)
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      int ent;
-      uint32_t off;
-      kpiece(j, ent, off);
-      __builtin_amdgcn_global_load_lds(kpool + (uint64_t)(uint32_t)pick(x.pg, ent) * page_bytes + head_off + off,
-                                       (lds_t*)(buf + (w * 2 + j) * 1024), 16, 0, 0);
+      asm volatile("" : "+v"(koff[j]));
+      __builtin_amdgcn_global_load_lds(kb + koff[j], (lds_t*)(buf + (w * 2 + j) * 1024), 16, 0, 0);
     }
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      int ent;
-      uint32_t off;
-      vpiece(j, ent, off);
-      __builtin_amdgcn_global_load_lds(vpool + (uint64_t)(uint32_t)pick(x.pg, ent) * page_bytes + head_off + off,
-                                       (lds_t*)(buf + KBYTES + (w * 2 + j) * 1024), 16, 0, 0);
+      asm volatile("" : "+v"(voff[j]));
+      __builtin_amdgcn_global_load_lds(vb + voff[j], (lds_t*)(buf + KBYTES + (w * 2 + j) * 1024), 16, 0, 0);
     }
   }
 };
@@ -1048,6 +1084,8 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf(AttnArgs a) {
   // seed operand is the key's mask bit times this (M::mask_a in two instructions)
   const int one_hi = hi == 0 ? M::bits(1.f) : 0;
   const Frag sel = rowsum_selector(lane);
+  TileAddr<P> ta;
+  ta.init(l32, hi);
 
   Frag qf[NQB][NDC];
   load_q(a, qbase, h, l32, hi, qf);
@@ -1091,7 +1129,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf(AttnArgs a) {
     auto qk_raw = [&](const char* b, int kb, int mi, floatx16 (&s)[NQB]) __attribute__((always_inline)) {
       Frag kf[NDC];
 #pragma unroll
-      for (int dc = 0; dc < NDC; ++dc) kf[dc] = read_k((const bf16*)b, 0, kb * 32 + l32, dc, hi);
+      for (int dc = 0; dc < NDC; ++dc) kf[dc] = ta.kop(b, kb, dc);
       u32x2 sw = {(uint32_t)(-((mi >> kb) & 1) & one_hi), 0u};
       const floatx16 s0 = M::mma_seed(__builtin_bit_cast(typename M::Seed, sw), M::mask_b(hi));
 #pragma unroll
@@ -1128,7 +1166,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf(AttnArgs a) {
       typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
       Frag kf[NDC];
 #pragma unroll
-      for (int dc = 0; dc < NDC; ++dc) kf[dc] = read_k((const bf16*)qbuf, 0, qkb * 32 + l32, dc, hi);
+      for (int dc = 0; dc < NDC; ++dc) kf[dc] = ta.kop(qbuf, qkb, dc);
       // softmax work of group g: the scaled logits and exponentials of
       // elements 2i, 2i + 1 of query block qb = g / 8 (pair g) and the bf16
       // pack of pair g - 1 (its exponentials issued a group earlier), so that
@@ -1185,7 +1223,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf(AttnArgs a) {
         if (g < 7) valu(g + 9);
         if (g < 4) {
           const int c = g >> 1, db = g & 1;
-          vfn[c][db] = read_v((const bf16*)(nvbuf + DL::KBYTES), 0, db * 32 + l32, nvkb, c, hi);
+          vfn[c][db] = ta.vop(nvbuf + DL::KBYTES, db, nvkb, c);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -1270,7 +1308,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf(AttnArgs a) {
 #pragma unroll
     for (int c = 0; c < NCH; ++c)
 #pragma unroll
-      for (int db = 0; db < 2; ++db) va[c][db] = read_v((const bf16*)(buf(0) + DL::KBYTES), 0, db * 32 + l32, 1, c, hi);
+      for (int db = 0; db < 2; ++db) va[c][db] = ta.vop(buf(0) + DL::KBYTES, db, 1, c);
 
     // one tile period; `use` holds the ids of tile t + 3, `next` receives those of t + 4
     auto period = [&](int i, typename DL::Ids& use, typename DL::Ids& next) __attribute__((always_inline)) {
