@@ -409,6 +409,9 @@ struct Mfma<bf16> {
   __device__ static inline floatx16 mma_seed(Seed a, Seed b) {
     return __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(a, b, zero16(), 0, 0, 0);
   }
+  __device__ static inline floatx16 mma_seed_acc(Seed a, Seed b, floatx16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(a, b, c, 0, 0, 0);
+  }
 };
 template <>
 struct Mfma<float> {
@@ -591,6 +594,20 @@ __device__ inline bool tile_partial(const i32x4& tl) {
 #pragma unroll
   for (int e = 0; e < EPT; ++e) any |= pick(tl, e) < P;
   return __builtin_amdgcn_readfirstlane(any) != 0;
+}
+
+// Whether 32-key block kb of a tile holds a masked key, from the entry
+// lengths in scalar registers (wave-uniform).
+template <int P>
+__device__ inline bool block_masked(const i32x4& tl, int kb) {
+  if constexpr (P <= 32) {
+    bool m = false;
+#pragma unroll
+    for (int e = kb * 32 / P; e < (kb + 1) * 32 / P; ++e) m = m || pick(tl, e) < P;
+    return m;
+  } else {
+    return tl.x < (kb + 1) * 32;
+  }
 }
 
 template <typename T, int P>
@@ -1117,6 +1134,10 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf(AttnArgs a) {
     // loop unrolled four times every buffer offset is a constant
     auto buf = [&](int i) __attribute__((always_inline)) { return lt + (i & 3) * BB; };
     // mask bits of a tile: bit kb set when key kb*32 + l32 is masked
+    // the same per block for the whole wave: bit kb set when block kb has a masked key
+    auto sminfo = [&](const typename DL::Ids& x) __attribute__((always_inline)) {
+      return (block_masked<P>(x.ln, 0) ? 1 : 0) | (block_masked<P>(x.ln, 1) ? 2 : 0);
+    };
     auto minfo = [&](const typename DL::Ids& x) __attribute__((always_inline)) {
       int r = 0;
 #pragma unroll
@@ -1160,7 +1181,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf(AttnArgs a) {
     // MFMAs while the next V^T fragments land.  The row sums of the new P go
     // to the matrix cores as well, one 16x16x32 product per packed operand, a
     // group after its last pack.
-    auto step = [&](const char* qbuf, int qkb, int qmi, const Frag (&vfc)[NCH][2], const char* nvbuf, int nvkb,
+    auto step = [&](const char* qbuf, int qkb, int qmi, int smi, const Frag (&vfc)[NCH][2], const char* nvbuf, int nvkb,
                     Frag (&vfn)[NCH][2], floatx16 (&sQ)[NQB], floatx16 (&sS)[NQB], Frag (&pS)[NCH][NQB],
                     const Frag (&pV)[NCH][NQB], floatx4 (&ts)[NQB]) __attribute__((always_inline)) {
       typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -1208,16 +1229,14 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf(AttnArgs a) {
         valu(g);
         __builtin_amdgcn_sched_barrier(0);
       }
-      // group 8: the mask product (all zero in a full tile)
-      u32x2 sw = {(uint32_t)(-((qmi >> qkb) & 1) & one_hi), 0u};
-      const floatx16 s0 = M::mma_seed(__builtin_bit_cast(typename M::Seed, sw), M::mask_b(hi));
+      // group 8: softmax work only
       valu(8);
       __builtin_amdgcn_sched_barrier(0);
-      // groups 9 .. 16: K.Q^T, the next V^T fragments read in the first four
+      // groups 9 .. 16: K.Q^T from zero, the next V^T fragments read in the first four
 #pragma unroll
       for (int g = 0; g < 8; ++g) {
         const int dc = g >> 1, qb = g & 1;
-        sQ[qb] = M::mma(kf[dc], qf[qb][dc], dc == 0 ? s0 : sQ[qb]);
+        sQ[qb] = dc == 0 ? M::mma(kf[dc], qf[qb][dc], zero16()) : M::mma(kf[dc], qf[qb][dc], sQ[qb]);
         if (g == 0) ts[0] = rowsum_mma(sel, pS[1][0], ts[0]);
         if (g == 4) ts[1] = rowsum_mma(sel, pS[0][1], floatx4{0.f, 0.f, 0.f, 0.f});
         if (g < 7) valu(g + 9);
@@ -1230,6 +1249,14 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf(AttnArgs a) {
       valu(16);
       __builtin_amdgcn_sched_barrier(0);
       ts[1] = rowsum_mma(sel, pS[1][1], ts[1]);
+      // a block with masked keys (wave-uniform): the mask product added to
+      // both query blocks' scores, pushing masked keys to about -1e30
+      if ((smi >> qkb) & 1) {
+        u32x2 sw = {(uint32_t)(-((qmi >> qkb) & 1) & one_hi), 0u};
+        const typename M::Seed sa = __builtin_bit_cast(typename M::Seed, sw), sb = M::mask_b(hi);
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb) sQ[qb] = M::mma_seed_acc(sa, sb, sQ[qb]);
+      }
     };
     // the sum check of block kb of buffer b after its softmax: if the sum of
     // some query's P over the block exceeds 2^16, the block's raw scores again (its tile is still in
@@ -1289,6 +1316,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf(AttnArgs a) {
     ld.issue(kp, vp, idc, buf(2), wave);
     // mask bits of tiles t, t + 1, t + 2 in bits 0-1, 2-3, 4-5
     int mr = minfo(ida) | minfo(idb) << 2 | minfo(idc) << 4;
+    int smr = sminfo(ida) | sminfo(idb) << 2 | sminfo(idc) << 4;
     idb = idd;  // the ids of tile t0 + 3, used in the first period
     asm volatile("" ::: "memory");
     wait_vmem<2 * DL::NISSUE>();  // tile t0 has landed
@@ -1316,7 +1344,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf(AttnArgs a) {
       // step 2i: P.V of block 1 of tile t - 1 (of tile t with P = 0 in the
       // first step), softmax of block 0 of tile t, QK of block 1 of tile t;
       // reads the V^T of block 0 of tile t for the next step
-      step(buf(i), 1, mr & 3, va, buf(i), 0, vb, s1, s0, p0, p1, ts);
+      step(buf(i), 1, mr & 3, smr & 3, va, buf(i), 0, vb, s1, s0, p0, p1, ts);
       settle(buf(i), 0, mr & 3, s0, p0, ts);
       // tile t + 1 has landed; tile t - 1's buffer is free: ids of tile t + 4,
       // data of tile t + 3 (past the split's end they are read and unused)
@@ -1329,12 +1357,14 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf(AttnArgs a) {
       ld.fetch(a, t + 4, next);
       ld.issue(kp, vp, use, buf(i + 3), wave);
       mr |= minfo(use) << 6;
+      smr |= sminfo(use) << 6;
       asm volatile("" ::: "memory");
       // step 2i + 1: P.V of block 0 of tile t, softmax of block 1 of tile t,
       // QK of block 0 of tile t + 1; reads the V^T of block 1 of tile t
-      step(buf(i + 1), 0, (mr >> 2) & 3, vb, buf(i), 1, va, s0, s1, p1, p0, ts);
+      step(buf(i + 1), 0, (mr >> 2) & 3, (smr >> 2) & 3, vb, buf(i), 1, va, s0, s1, p1, p0, ts);
       settle(buf(i), 1, mr & 3, s1, p1, ts);
       mr >>= 2;
+      smr >>= 2;
     };
     // after the prologue idb holds the ids of tile t0 + 3
     for (int i = 0; i < n; i += 4) {
