@@ -503,22 +503,17 @@ __device__ inline bf16x8 pack_p(const floatx16& s, int ch, bf16) {
 __device__ inline float pack_p(const floatx16& s, int ch, float) { return s[ch]; }
 
 // Queries (already rotated) as B operands: lane holds query qb*32 + l32,
-// dims [dc*2*KPL + hi*KPL, +KPL).
+// dims [dc*2*KPL + hi*KPL, +KPL).  Lanes past the last query read the last
+// one (no branch, so no load waits for another): their columns are computed
+// and never written.
 __device__ inline void load_q(const AttnArgs& a, int qbase, int h, int l32, int hi, bf16x8 (&qf)[2][4]) {
   const bf16* Q = (const bf16*)a.q;
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
-    int q = qbase + qb * 32 + l32;
+    const int q = min(qbase + qb * 32 + l32, a.Tq - 1);
 #pragma unroll
-    for (int dc = 0; dc < 4; ++dc) {
-      Vec16<bf16> v;
-      v.u = make_uint4(0, 0, 0, 0);
-      if (q < a.Tq) v.u = *(const uint4*)(Q + ((size_t)q * a.H + h) * kHeadDim + dc * 16 + hi * 8);
-      bf16x8 f;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) f[i] = v.e[i];
-      qf[qb][dc] = f;
-    }
+    for (int dc = 0; dc < 4; ++dc)
+      qf[qb][dc] = *(const bf16x8*)(Q + ((size_t)q * a.H + h) * kHeadDim + dc * 16 + hi * 8);
   }
 }
 __device__ inline void load_q(const AttnArgs& a, int qbase, int h, int l32, int hi, float (&qf)[1][32]) {
@@ -794,6 +789,10 @@ __device__ inline void wait_vmem() {
   static_assert(N >= 0 && N < 16, "vmcnt immediate");
   __builtin_amdgcn_s_waitcnt(0x0F70 | N);
 }
+
+// s_waitcnt on the scalar-memory / LDS count only (lgkmcnt 0; vmcnt 63 and
+// expcnt 7: no wait)
+__device__ inline void wait_smem() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
 // max over the two 32-lane halves of the wave
 __device__ inline float half_swap_max(float x) {
@@ -1301,11 +1300,9 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf(AttnArgs a) {
     ld.fetch(a, t0 + 1, idb);
     ld.fetch(a, t0 + 2, idc);
     ld.fetch(a, t0 + 3, idd);
-    __builtin_amdgcn_s_waitcnt(0);  // the queries and the ids
-#pragma unroll
-    for (int qb = 0; qb < NQB; ++qb)
-#pragma unroll
-      for (int dc = 0; dc < NDC; ++dc) asm volatile("" : "+v"(qf[qb][dc]));
+    // the ids only: the queries' vector loads land with tile t0's (loads
+    // return in order, and the queries were issued first)
+    wait_smem();
     ready(ida);
     ready(idb);
     ready(idc);
@@ -1319,7 +1316,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf(AttnArgs a) {
     int smr = sminfo(ida) | sminfo(idb) << 2 | sminfo(idc) << 4;
     idb = idd;  // the ids of tile t0 + 3, used in the first period
     asm volatile("" ::: "memory");
-    wait_vmem<2 * DL::NISSUE>();  // tile t0 has landed
+    wait_vmem<2 * DL::NISSUE>();  // the queries and tile t0 have landed
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
