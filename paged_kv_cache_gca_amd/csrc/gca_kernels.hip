@@ -1171,15 +1171,16 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf(AttnArgs a) {
     };
     // One step: P.V of pV with the V^T fragments vfc (read during the
     // previous step), softmax of sS into pS, K.Q^T of block qkb of buffer
-    // qbuf into sQ (mask bits qmi), and the V^T fragments of the next step's
-    // P.V (block nvkb of buffer nvbuf) into vfn.  Issued in 17 groups, each an
-    // MFMA and five VALU instructions of the softmax (two elements: their
-    // scaled logits and exponentials, one bf16 pack), kept in this order by
-    // scheduling barriers: the eight P.V MFMAs first, while this step's K
-    // fragments land, then the mask product (no LDS operand), then the K.Q^T
-    // MFMAs while the next V^T fragments land.  The row sums of the new P go
-    // to the matrix cores as well, one 16x16x32 product per packed operand, a
-    // group after its last pack.
+    // qbuf into sQ (mask bits qmi per lane, smi per wave), and the V^T
+    // fragments of the next step's P.V (block nvkb of buffer nvbuf) into vfn.
+    // Issued in 17 groups of five VALU instructions of the softmax (two
+    // elements: their scaled logits and exponentials, one bf16 pack), each but
+    // group 8 with an MFMA, kept in this order by scheduling barriers: the
+    // eight P.V MFMAs first, while this step's K fragments land, then the
+    // K.Q^T MFMAs while the next V^T fragments land.  The row sums of the new
+    // P go to the matrix cores as well, one 16x16x32 product per packed
+    // operand, a group after its last pack.  A block with a masked key adds
+    // the mask product to its scores at the end.
     auto step = [&](const char* qbuf, int qkb, int qmi, int smi, const Frag (&vfc)[NCH][2], const char* nvbuf, int nvkb,
                     Frag (&vfn)[NCH][2], floatx16 (&sQ)[NQB], floatx16 (&sS)[NQB], Frag (&pS)[NCH][NQB],
                     const Frag (&pV)[NCH][NQB], floatx4 (&ts)[NQB]) __attribute__((always_inline)) {
