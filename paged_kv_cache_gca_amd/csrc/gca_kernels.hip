@@ -357,16 +357,18 @@ __global__ void k_ring_init(int32_t* ring, const int32_t* init, int N) {
 // ---------------------------------------------------------------------------
 // Paged attention.
 //
-// Workgroup = 4 waves x 64 queries of one head, over one split of the gather
-// list.  Per 64-key tile: K (64 keys x 64 dims) and V^T (64 dims x 64 keys)
-// are staged in LDS, then each wave computes S^T = K Q^T (keys x queries) with
-// 32x32 MFMA blocks, so that each lane owns one query column: the softmax max
-// and scaling are per lane plus one exchange with lane ^ 32.  P^T is fed
+// Workgroup = 4 waves x 64 queries (32 with the fp32 cache) of one head,
+// over one split of the gather list.  Per 64-key tile: K (64 keys x 64 dims)
+// and V^T (64 dims x 64 keys) are staged in LDS, then each wave computes
+// S^T = K Q^T (keys x queries) with 32x32 MFMA blocks, so that each lane owns
+// one query column: the softmax max and scaling are per lane plus one
+// exchange with lane ^ 32.  P^T is fed
 // straight from the S^T accumulators as the B operand of O^T = V^T P^T; the
 // key order inside each 16-key chunk follows the accumulator layout, and the
-// V^T operand is read in the same order.  Row sums are dot products of the
-// same rounded P with ones, so sum(P) and P.V use identical weights (they
-// sum to one exactly, so an offset common to all V rows passes through).
+// V^T operand is read in the same order.  Row sums add the same rounded P
+// that P.V uses (on the matrix cores in the bf16 kernel), so sum(P) and P.V
+// use identical weights (they sum to one, so an offset common to all V rows
+// passes through).
 
 template <typename T>
 struct Mfma;
@@ -378,11 +380,12 @@ __device__ inline floatx16 zero16() {
   return z;
 }
 
-// Partial tiles start each 32-key block's S^T accumulators from a rank-1
-// mask product instead of zero: A holds, per key row, 1 for a key past its
-// gather entry's valid length (else 0) in column 0; B holds -1e30 in row 0 for
-// every query column.  A masked key's score is then about -1e30, its logit
-// -inf in effect, its P exactly 0.
+// A 32-key block with a masked key gets a rank-1 mask product in its S^T
+// accumulators (the fp32 kernel starts from it, the bf16 kernel adds it after
+// K.Q^T): A holds, per key row, 1 for a key past its gather entry's valid
+// length (else 0) in column 0; B holds -1e30 in row 0 for every query column.
+// A masked key's score is then about -1e30, its logit -inf in effect, its P
+// exactly 0.
 constexpr float kMaskedScore = -1e30f;
 typedef short shortx4 __attribute__((ext_vector_type(4)));
 
@@ -1096,8 +1099,8 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf(AttnArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hi = lane >> 5;
   const int qbase = (qt * kWaves + wave) * 64;
-  // bf16 1.0 in the lanes that hold column 0 of a seed A operand, else 0: a
-  // seed operand is the key's mask bit times this (M::mask_a in two instructions)
+  // bf16 1.0 in the lanes that hold column 0 of a mask-product A operand, else
+  // 0: that operand is the key's mask bit times this (M::mask_a in two instructions)
   const int one_hi = hi == 0 ? M::bits(1.f) : 0;
   const Frag sel = rowsum_selector(lane);
   TileAddr<P> ta;
