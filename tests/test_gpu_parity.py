@@ -217,6 +217,34 @@ def test_frame1004_stream_through_gca_step_sampled():
     p.check_state()
 
 
+def test_frame1004_p32_stream_through_gca_step_sampled():
+    """The 1004-token, 16-head frame at P=32 (two gather entries per 64-key
+    tile, each frame's last page partial) through gca_step, every other frame a
+    non-keyframe (appended, attended, rolled back), several splits per (head,
+    q tile): sampled rows against the oracle at the start, around the first
+    evictions and at the end; bookkeeping bit-exact at the end."""
+    w = WL.Workload("bf16_T1004_H16_P32_W8_kf2_40f", T=1004, H=16, D=64, P=32, dtype="bf16",
+                    n_frames=40, A=1, W=8, C=13, rope=1, num_special=5, grid_h=27, grid_w=37,
+                    keyframe_interval=2, seed=11)
+    p = Pair(w)
+    rows = _rows(w.T, seed=4)
+    out = torch.empty((w.T, w.H, w.D), dtype=torch.float32, device="cuda")
+    lse = torch.empty((w.T, w.H), dtype=torch.float32, device="cuda")
+    for f in range(w.n_frames):
+        key = w.is_keyframe(f)
+        k, v, kd, vd = p.kv(f)
+        q = p.fs.q(f)
+        assert p.gpu.step(f, kd, vd, dev(q, w.dtype), out, lse, keyframe=key) == 0
+        assert p.orc.append(f, k, v, temp=not key) == 0
+        if key:
+            assert p.orc.evict() == 0
+        if f in (0, 1, 17, 18, 19, 38, 39):
+            _cmp_outputs(p, f, q, out, lse, rows)
+        if not key:
+            assert p.orc.rollback(f) == 0
+    p.check_state()
+
+
 @pytest.mark.parametrize("w,last,samples", [
     (WL.STREAM1000_W64, 100, (64, 65, 100)),
     (WL.STREAM10K_KF4, 150, (132, 148, 149, 150)),
