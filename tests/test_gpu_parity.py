@@ -160,7 +160,7 @@ def test_keep_every_token_and_window_never_full():
     (2, 3, 64, "bf16", 0, 2, 0, 1, 1, 1, 1, 2),    # one special + one patch token, no anchor, no trajectory
     (17, 1, 16, "bf16", 2, 1, 17, 1, 2, 3, 5, 1),  # ragged page, C = T, window of one frame
     (33, 5, 32, "f32", 1, 3, 4, 1, 0, 3, 11, 3),   # odd head count, TEMP frames
-    (3, 5, 16, "bf16", 1, 4, 2, 1, 2, 1, 1, 1),    # three query rows: the decode kernel
+    (3, 5, 16, "bf16", 1, 4, 2, 1, 2, 1, 1, 1),    # three query rows in a 64-query wave
     (4, 2, 32, "f32", 1, 2, 1, 1, 0, 2, 2, 2),     # four query rows, fp32, TEMP frames
 ])
 def test_degenerate_shapes(T, H, P, dtype, A, W, C, rope, ns, gh, gw, interval):
@@ -634,7 +634,7 @@ def _attend_frames(p, first, nf):
     (300, 4, 16, "bf16", 4, 4, 1, 3, 9, 33, False, "f32", False),   # several q tiles, ragged tail
     (300, 4, 64, "bf16", 4, 2, 1, 3, 9, 33, False, "f32", True),    # the last two of four anchors
     (300, 12, 32, "bf16", 3, 3, 1, 3, 9, 33, False, "bf16", False), # H not a multiple of 8, bf16 out
-    (2, 3, 16, "bf16", 2, 2, 1, 1, 1, 1, False, "f32", True),        # 2 x 2 query rows: decode kernel
+    (2, 3, 16, "bf16", 2, 2, 1, 1, 1, 1, False, "f32", True),        # 2 x 2 query rows
     (1004, 16, 16, "bf16", 8, 8, 1, 5, 27, 37, True, "f32", True),  # 8 scale frames at the frame shape
     (1004, 16, 64, "bf16", 4, 4, 1, 5, 27, 37, True, "f32", False),
 ])
